@@ -1,0 +1,200 @@
+// Host side of libmla.so: argument checks (all before any HIP call), the split planner, the
+// per-device compute-unit cache and the kernel launches.  See include/mla.h for the contract.
+#include <math.h>
+#include <mutex>
+
+#include "internal.h"
+#include "mla.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+mla_status device_cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::call_once(g_cu_once[dev], [dev] {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
+    g_cu_count[dev] = v;
+  });
+  if (g_cu_count[dev] <= 0) return MLA_ERR_HIP;
+  *out = g_cu_count[dev];
+  return MLA_OK;
+}
+
+bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Planner cost model.  Work is MFMA-bound per workgroup and HBM-bound overall; every split
+// adds one fp32 partial row per query row (written by the decode kernel, read back by the
+// combine), and every extra row group per split re-reads the split's KV from L2.  Estimates
+// are in nanoseconds on round numbers for an MI355X-class part (8 TB/s HBM, ~30 TB/s L2,
+// ~3.5 PFLOP/s of sustained FP8 MFMA); only their ratios matter.
+double plan_cost(int64_t B, int64_t M, int64_t L, int cu, int rows_per_group, int64_t S) {
+  const int64_t G = cdiv(M, rows_per_group);
+  const int64_t tiles = cdiv(L, 32);
+  const int64_t per = cdiv(tiles, S);                       // tiles per chunk
+  const int64_t wgs = B * S * G;
+  const double waves = (double)cdiv(wgs, cu);               // workgroup rounds per CU
+  const double kv = (double)B * L * 576.0;
+  const double t_hbm = kv / 8.0e3;                          // bytes / (bytes per ns)
+  const double t_l2 = kv * (double)G / 30.0e3;
+  // per workgroup: per tiles of 32 tokens x rows_per_group rows, QK + hi/lo PV flops
+  const double wg_flops = (double)per * 32.0 * rows_per_group * 2.0 * (576.0 + 1024.0);
+  const double t_mfma = waves * wg_flops / (3.5e6 / cu);    // flops / (flops per ns per CU)
+  const double partial = (double)B * S * M * 513.0 * 4.0 * 2.0;  // write + read back
+  const double t_part = partial / 6.0e3;
+  double t = t_hbm;
+  if (t_l2 > t) t = t_l2;
+  if (t_mfma > t) t = t_mfma;
+  return t + t_part + 2000.0 * (S > 1);                     // + combine launch
+}
+
+mla_status plan(int batch, int q_tokens, int heads, int max_seq_len, int cu, int* splits,
+                int* rows_per_group) {
+  const int64_t M = (int64_t)q_tokens * heads;
+  const int64_t tiles = cdiv(max_seq_len, 32);
+  double best = -1.0;
+  int best_s = 1, best_r = 128;
+  // 128-row groups are supported by the kernel but not chosen: that variant still spills
+  // Q fragments to scratch, which drains the KV DMA pipeline.
+  for (int r : {32, 64}) {
+    const int tl = 128 / r;  // waves of a workgroup that stream different tiles
+    // at least one stage of tiles per wave per chunk, at most the CU count of workgroups
+    const int64_t s_max = tiles / tl > 0 ? tiles / tl : 1;
+    for (int64_t S = 1; S <= s_max && S <= 4096; S = S < 8 ? S + 1 : S + S / 8) {
+      const double c = plan_cost(batch, M, max_seq_len, cu, r, S);
+      if (best < 0.0 || c < best) {
+        best = c;
+        best_s = (int)S;
+        best_r = r;
+      }
+    }
+  }
+  *splits = best_s;
+  *rows_per_group = best_r;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t n, float scale,
+                                void* stream) {
+  if (n < 0 || !good_scale(scale)) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (src_dev == nullptr || dst_dev == nullptr) return MLA_ERR_INVALID_ARG;
+  const hipError_t e = mla::launch_quantize(src_dev, dst_dev, n, scale, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len, int cu_count,
+                            int* num_splits, int* rows_per_group, int64_t* partial_rows) {
+  if (batch < 1 || q_tokens < 1 || heads < 1 || max_seq_len < 1 || cu_count < 0)
+    return MLA_ERR_INVALID_ARG;
+  if ((int64_t)q_tokens * heads > mla::kMaxRows) return MLA_ERR_UNSUPPORTED;
+  int cu = cu_count;
+  if (cu == 0) {
+    const mla_status st = device_cu_count(&cu);
+    if (st != MLA_OK) return st;
+  }
+  int s = 1, r = 128;
+  plan(batch, q_tokens, heads, max_seq_len, cu, &s, &r);
+  if (num_splits) *num_splits = s;
+  if (rows_per_group) *rows_per_group = r;
+  if (partial_rows) *partial_rows = (int64_t)batch * s * q_tokens * heads;
+  return MLA_OK;
+}
+
+mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                              const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                              int batch, int q_tokens, int heads, int page_size, int max_pages,
+                              int max_seq_len, float q_scale, float kv_scale, float softmax_scale,
+                              int num_splits, int rows_per_group, float* partial_o_dev,
+                              float* partial_lse_dev, int64_t partial_rows_capacity,
+                              void* stream) {
+  if (batch < 0 || q_tokens < 1 || heads < 1 || page_size < 1 || max_pages < 1 ||
+      num_splits < 0 || rows_per_group < 0 || partial_rows_capacity < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!good_scale(q_scale) || !good_scale(kv_scale) || !good_scale(softmax_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!q8_dev || !kv_pool_dev || !page_table_dev || !seq_lens_dev || !partial_o_dev ||
+      !partial_lse_dev)
+    return MLA_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)q_tokens * heads;
+  if (M > mla::kMaxRows || page_size % mla::kTile != 0 ||
+      (int64_t)max_pages * page_size > 0x7FFFFFFFLL - 64)
+    return MLA_ERR_UNSUPPORTED;
+  if (rows_per_group != 0 && rows_per_group != 32 && rows_per_group != 64 &&
+      rows_per_group != 128)
+    return MLA_ERR_UNSUPPORTED;
+  int S = num_splits, r = rows_per_group;
+  if (S == 0 || r == 0) {
+    if (max_seq_len < 1) return MLA_ERR_INVALID_ARG;
+    int cu = 0;
+    const mla_status st = device_cu_count(&cu);
+    if (st != MLA_OK) return st;
+    int ps = 1, pr = 128;
+    plan(batch, q_tokens, heads, max_seq_len, cu, &ps, &pr);
+    if (S == 0) S = ps;
+    if (r == 0) r = pr;
+  }
+  if (S > 65535) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * S * M > partial_rows_capacity) return MLA_ERR_WORKSPACE;
+  const int64_t groups = cdiv(M, r);
+  if (cdiv((int64_t)batch * S, 8) * 8 * groups > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+
+  mla::DecodeParams p;
+  p.q8 = q8_dev;
+  p.kv = kv_pool_dev;
+  p.page_table = page_table_dev;
+  p.seq_lens = seq_lens_dev;
+  p.partial_o = partial_o_dev;
+  p.partial_lse = partial_lse_dev;
+  p.batch = batch;
+  p.q_tokens = q_tokens;
+  p.heads = heads;
+  p.rows = (int)M;
+  p.page_size = page_size;
+  p.max_pages = max_pages;
+  p.num_splits = S;
+  p.groups = (int)groups;
+  p.c2 = (float)((double)q_scale * kv_scale * softmax_scale * 1.4426950408889634);
+  p.kv_scale = kv_scale;
+  const hipError_t e = mla::launch_decode(p, r, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_splitkv_combine(const float* partial_o_dev, const float* partial_lse_dev,
+                               int batch, int num_splits, int q_tokens, int heads,
+                               uint16_t* out_bf16_dev, float* out_lse_dev, void* stream) {
+  if (batch < 0 || num_splits < 1 || q_tokens < 1 || heads < 1) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!partial_o_dev || !partial_lse_dev || !out_bf16_dev) return MLA_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)q_tokens * heads;
+  if (M > mla::kMaxRows || num_splits > mla::kMaxSplitsCombine) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * M * 2 > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+  const hipError_t e = mla::launch_combine(partial_o_dev, partial_lse_dev, batch, num_splits,
+                                           (int)M, out_bf16_dev, out_lse_dev,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

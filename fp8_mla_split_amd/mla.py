@@ -1,0 +1,164 @@
+"""ctypes binding of libmla.so: argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels.  PyTorch provides device memory
+(``tensor.data_ptr()``) and the stream (``torch.cuda.current_stream()``); outputs that the
+caller does not pass are allocated with torch.  Names follow ``include/mla.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libmla.so")
+if not os.path.exists(lib_path):
+    raise ImportError(f"{lib_path} is not built; run `python -m fp8_mla_split_amd.build`")
+_lib = ctypes.CDLL(lib_path)
+
+_i32, _i64, _f32, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_lib.mla_status_string.restype = ctypes.c_char_p
+_lib.mla_status_string.argtypes = [_i32]
+_lib.mla_quantize_fp8_sat.restype = _i32
+_lib.mla_quantize_fp8_sat.argtypes = [_vp, _vp, _i64, _f32, _vp]
+_lib.mla_splitkv_plan.restype = _i32
+_lib.mla_splitkv_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32),
+                                  ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
+_lib.mla_decode_splitkv.restype = _i32
+_lib.mla_decode_splitkv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    _f32, _f32, _f32, _i32, _i32, _vp, _vp, _i64, _vp]
+_lib.mla_splitkv_combine.restype = _i32
+_lib.mla_splitkv_combine.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+
+D_KV, D_V = 576, 512
+
+
+class MLAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)}")
+
+
+def status_string(code: int) -> str:
+    return _lib.mla_status_string(int(code)).decode()
+
+
+def _check(code: int, where: str) -> None:
+    if code != 0:
+        raise MLAError(code, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev_tensor(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on the GPU")
+
+
+@dataclass(frozen=True)
+class Plan:
+    num_splits: int
+    rows_per_group: int
+    partial_rows: int
+
+
+def quantize_fp8_sat(x: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None):
+    """e4m3 codes (uint8, same shape) of ``x / scale`` with saturation to +-448."""
+    _dev_tensor(x, torch.float32, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _dev_tensor(out, torch.uint8, "out")
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
+    _check(_lib.mla_quantize_fp8_sat(_ptr(x), _ptr(out), x.numel(), float(scale),
+                                     _stream(x.device)), "mla_quantize_fp8_sat")
+    return out
+
+
+def splitkv_plan(batch: int, q_tokens: int, heads: int, max_seq_len: int,
+                 cu_count: int = 0) -> Plan:
+    s, r, n = _i32(), _i32(), _i64()
+    _check(_lib.mla_splitkv_plan(batch, q_tokens, heads, max_seq_len, cu_count,
+                                 ctypes.byref(s), ctypes.byref(r), ctypes.byref(n)),
+           "mla_splitkv_plan")
+    return Plan(s.value, r.value, n.value)
+
+
+def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.Tensor,
+                   seq_lens: torch.Tensor, q_scale: float, kv_scale: float,
+                   softmax_scale: float, max_seq_len: int, num_splits: int = 0,
+                   rows_per_group: int = 0, partial_o: Optional[torch.Tensor] = None,
+                   partial_lse: Optional[torch.Tensor] = None):
+    """Split-KV partial attention.  Returns ``(partial_o, partial_lse, num_splits)``.
+
+    q8 [B, Sq, H, 576] uint8; kv_pool8 [pages, page_size, 576] uint8; page_table
+    [B, max_pages] int32; seq_lens [B] int32.  partial_o [B, S, Sq*H, 512] fp32 and
+    partial_lse [B, S, Sq*H] fp32 are allocated when not given.
+    """
+    _dev_tensor(q8, torch.uint8, "q8")
+    _dev_tensor(kv_pool8, torch.uint8, "kv_pool8")
+    _dev_tensor(page_table, torch.int32, "page_table")
+    _dev_tensor(seq_lens, torch.int32, "seq_lens")
+    B, Sq, H, d = q8.shape
+    if d != D_KV or kv_pool8.dim() != 3 or kv_pool8.shape[2] != D_KV:
+        raise ValueError("q8 and kv_pool8 rows must be 576 wide")
+    page_size = kv_pool8.shape[1]
+    if num_splits == 0 or rows_per_group == 0:
+        plan = splitkv_plan(B, Sq, H, max_seq_len)
+        num_splits = num_splits or plan.num_splits
+        rows_per_group = rows_per_group or plan.rows_per_group
+    rows = Sq * H
+    if partial_o is None:
+        partial_o = torch.empty((B, num_splits, rows, D_V), dtype=torch.float32,
+                                device=q8.device)
+    if partial_lse is None:
+        partial_lse = torch.empty((B, num_splits, rows), dtype=torch.float32, device=q8.device)
+    _dev_tensor(partial_o, torch.float32, "partial_o")
+    _dev_tensor(partial_lse, torch.float32, "partial_lse")
+    cap = min(partial_o.numel() // D_V, partial_lse.numel())
+    _check(_lib.mla_decode_splitkv(
+        _ptr(q8), _ptr(kv_pool8), _ptr(page_table), _ptr(seq_lens), B, Sq, H, page_size,
+        page_table.shape[1], max_seq_len, float(q_scale), float(kv_scale),
+        float(softmax_scale), num_splits, rows_per_group, _ptr(partial_o), _ptr(partial_lse),
+        cap, _stream(q8.device)), "mla_decode_splitkv")
+    return partial_o, partial_lse, num_splits
+
+
+def splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens: int,
+                    heads: int, out: Optional[torch.Tensor] = None,
+                    out_lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """LSE merge -> (out [B, Sq, H, 512] bf16, lse [B, Sq, H] fp32 or None)."""
+    _dev_tensor(partial_o, torch.float32, "partial_o")
+    _dev_tensor(partial_lse, torch.float32, "partial_lse")
+    B, S = partial_lse.shape[0], partial_lse.shape[1]
+    if partial_lse.shape[2] != q_tokens * heads or partial_o.shape[:3] != partial_lse.shape:
+        raise ValueError("partial shapes do not match [B, S, Sq*H(, 512)]")
+    dev = partial_o.device
+    if out is None:
+        out = torch.empty((B, q_tokens, heads, D_V), dtype=torch.bfloat16, device=dev)
+    if out_lse is None and want_lse:
+        out_lse = torch.empty((B, q_tokens, heads), dtype=torch.float32, device=dev)
+    _dev_tensor(out, torch.bfloat16, "out")
+    if out_lse is not None:
+        _dev_tensor(out_lse, torch.float32, "out_lse")
+    _check(_lib.mla_splitkv_combine(_ptr(partial_o), _ptr(partial_lse), B, S, q_tokens, heads,
+                                    _ptr(out), _ptr(out_lse), _stream(dev)),
+           "mla_splitkv_combine")
+    return out, out_lse
+
+
+def decode(q8, kv_pool8, page_table, seq_lens, q_scale, kv_scale, softmax_scale, max_seq_len,
+           num_splits: int = 0, rows_per_group: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Partial attention followed by the combine: (out bf16, lse fp32)."""
+    po, pl, _ = decode_splitkv(q8, kv_pool8, page_table, seq_lens, q_scale, kv_scale,
+                               softmax_scale, max_seq_len, num_splits, rows_per_group)
+    return splitkv_combine(po, pl, q8.shape[1], q8.shape[2])

@@ -1,0 +1,152 @@
+/*
+ * mla.h -- C ABI of libmla.so: FP8 MLA split-KV decode for AMD Instinct MI355X (gfx950).
+ *
+ * Sources cited below:
+ *   [A]      the arex-research.com page "SGLang 与 Miles 团队称在预发布 Vera Rubin 上跑通
+ *            Kimi K3 推理和端到端 RL，自测 FP8 MLA 提速最高约 20%".
+ *   [A/MLA]  its section "Kimi K3 的 MLA：更深的流水线、更快的 split-KV 归约"; the section's
+ *            list has four items: (1) deeper MLA pipeline, (2) faster split-KV reduction,
+ *            (3) 64-way split-KV, (4) native saturating FP8 conversion.
+ *   [B]      the ai.newsbites.today page "LMSYS、NVIDIA Rubin向けの高速化成果を発表", section
+ *            "MLAアテンションのパイプライン深化".
+ *
+ * Problem (the pages' statement, in our words): long-context MLA decode mostly waits on
+ * reading the KV cache from HBM ([A/MLA] (1), [B]).  Q and KV are first converted to FP8
+ * with a saturating cast ([A/MLA] (4)); at low batch one request's KV is split over many
+ * workgroups, each producing a partial result, and a second kernel merges the partials
+ * ([A/MLA] (2), (3)).  The KV row is 576 bytes wide (512 latent + 64 rope columns, shared
+ * by all query heads); the value vector is the row's first 512 columns.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers (HIP device memory); everything else is
+ *     passed by value.  The caller allocates and frees every buffer; the library never
+ *     allocates, frees or synchronises.  Its only state is a per-device cache of the
+ *     compute-unit count, filled on first use.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Work is
+ *     enqueued asynchronously; device-side faults surface at the caller's next sync.
+ *   - Every argument check runs before any HIP call, so invalid arguments are reported
+ *     on a host without a GPU.  Nothing throws across the ABI and nothing aborts.
+ *   - FP8 here is OCP E4M3 without infinities (max 448, NaN = S.1111.111), the format
+ *     gfx950's conversion and matrix instructions use.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer where one is required, negative size, non-finite
+                              or non-positive scale */
+  MLA_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported shapes (see each call) */
+  MLA_ERR_WORKSPACE = 3,   /* partial buffers too small for the requested split count */
+  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mla_status_string(mla_status s);
+
+/*
+ * Saturating FP8 quantisation of a contiguous fp32 array ([A/MLA] item (4)).
+ *
+ *   dst_dev[i] = e4m3_sat_rne(float32(src_dev[i]) / scale)   for i in [0, n)
+ *
+ * The quotient is an IEEE fp32 division.  It is rounded to the nearest E4M3 value, ties to
+ * the even code.  Every finite |quotient| >= 448 and +-inf saturate to 0x7E | sign (never
+ * NaN); NaN becomes 0x7F | sign; the sign of zero is kept.  With a per-tensor scale
+ * amax / 448 the largest magnitude maps to 448.
+ *   src_dev : fp32 [n], device.        dst_dev : uint8 [n], device (may not alias src_dev).
+ *   n       : element count, >= 0 (0 enqueues nothing).
+ *   scale   : finite, > 0.
+ * Errors: INVALID_ARG for n < 0, a NULL pointer with n > 0, or a bad scale; HIP on launch
+ * failure.
+ */
+mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t n, float scale,
+                                void* stream);
+
+/*
+ * Split planner ([A/MLA] item (3): at batch 1 a fixed split count leaves most compute units
+ * idle; the count has to follow the machine and the shape).  Chooses, from the compute-unit
+ * count, the batch, the number of query rows (q_tokens * heads) and the longest context:
+ *   *num_splits      S, the number of KV chunks per request (>= 1);
+ *   *rows_per_group  query rows handled by one workgroup: 32, 64 or 128.  Rows are the
+ *                    (query token, head) pairs of a request in [Sq, H] order; a request's
+ *                    rows are covered by ceil(Sq*H / rows_per_group) workgroups per chunk,
+ *                    which read the chunk's KV through the same L2;
+ *   *partial_rows    B * S * Sq * H: the entries mla_decode_splitkv writes, i.e. the sizes
+ *                    of partial_o (x 512 floats) and partial_lse (x 1 float).
+ *   cu_count : compute units to plan for; 0 queries the current device (a HIP call).
+ * Any output pointer may be NULL.  Errors: INVALID_ARG for batch, q_tokens, heads or
+ * max_seq_len < 1 or cu_count < 0; UNSUPPORTED when q_tokens * heads > 65536.
+ */
+mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len, int cu_count,
+                            int* num_splits, int* rows_per_group, int64_t* partial_rows);
+
+/*
+ * Split-KV partial attention over an FP8 paged KV cache ([A/MLA] items (1)-(3), [B]).
+ *
+ * For request b, query token t and head h (row r = t * H + h), and for chunk s of the
+ * request's tokens, computes over the positions n of that chunk that the row may see
+ * (bottom-right causal: n <= L_b - Sq + t, with L_b = seq_lens_dev[b] counting the Sq query
+ * tokens):
+ *   z_n  = softmax_scale * q_scale * kv_scale * (dec(Q8[b,t,h,:]) . dec(KV8[n,:]))
+ *   partial_lse[b,s,r]    = log(sum_n exp(z_n))          (natural log; -inf if no position)
+ *   partial_o[b,s,r,0:512] = sum_n softmax(z)_n * kv_scale * dec(KV8[n,0:512])
+ * Chunk s holds tiles [s*c, (s+1)*c) of 32 tokens, c = ceil(ceil(L_b/32) / S).  Partial
+ * outputs are fp32; where the lse is -inf (empty chunk, or no visible position) the
+ * partial_o entry is unspecified.
+ *
+ * Layouts (all contiguous, row-major):
+ *   q8_dev          uint8 [B, Sq, H, 576]          e4m3 codes of Q
+ *   kv_pool_dev     uint8 [num_pages, page_size, 576]  e4m3 codes of the latent+rope KV
+ *   page_table_dev  int32 [B, max_pages]   logical token n of request b is row n % page_size
+ *                                          of page page_table[b, n / page_size]
+ *   seq_lens_dev    int32 [B]              context length per request (device values are
+ *                                          clamped to [0, max_pages * page_size])
+ *   partial_o_dev   fp32 [B, S, Sq*H, 512];  partial_lse_dev fp32 [B, S, Sq*H]
+ * A contiguous per-request cache is the same call with page_size = the padded length and
+ * page_table[b] = {b}.
+ *   max_seq_len   : host upper bound of the lengths, used only when num_splits == 0.
+ *   num_splits    : S >= 1, or 0 to take the planner's choice for (B, Sq, H, max_seq_len).
+ *   rows_per_group: 32, 64 or 128, or 0 to take the planner's choice.
+ *   partial_rows_capacity : entries the partial buffers hold (see mla_splitkv_plan).
+ * Supported: 1 <= Sq, Sq*H <= 65536, page_size a positive multiple of 32, max_pages >= 1.
+ * Errors: INVALID_ARG (NULL pointers with B > 0, negative sizes, scales not finite and > 0);
+ * UNSUPPORTED (shape outside the supported set); WORKSPACE (B*S*Sq*H > capacity); HIP.
+ * B == 0 enqueues nothing.
+ */
+mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                              const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                              int batch, int q_tokens, int heads, int page_size, int max_pages,
+                              int max_seq_len, float q_scale, float kv_scale, float softmax_scale,
+                              int num_splits, int rows_per_group,
+                              float* partial_o_dev, float* partial_lse_dev,
+                              int64_t partial_rows_capacity, void* stream);
+
+/*
+ * Log-sum-exp merge of the split partials ([A/MLA] item (2)).  For each (b, r):
+ *   M = max_s lse_s;  w_s = exp(lse_s - M);  O = sum_s w_s O_s / sum_s w_s;
+ *   lse = M + log(sum_s w_s)
+ * Splits with lse_s = -inf are skipped (their partial_o is never read as a weight);
+ * a row whose splits are all empty gives O = 0 and lse = -inf.  Each workgroup issues all
+ * of a row's partial loads before it accumulates them in registers.
+ *   partial_o_dev fp32 [B, S, R, 512], partial_lse_dev fp32 [B, S, R] with R = Sq * H;
+ *   out_bf16_dev  uint16 [B, Sq, H, 512]: bf16 bit patterns, round-to-nearest-even;
+ *   out_lse_dev   fp32 [B, Sq, H] or NULL.
+ * Errors: INVALID_ARG (NULL inputs/outputs with B > 0, sizes < 1); UNSUPPORTED (S > 4096 or
+ * Sq*H > 65536); HIP.  B == 0 enqueues nothing.
+ */
+mla_status mla_splitkv_combine(const float* partial_o_dev, const float* partial_lse_dev,
+                               int batch, int num_splits, int q_tokens, int heads,
+                               uint16_t* out_bf16_dev, float* out_lse_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

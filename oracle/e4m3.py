@@ -57,32 +57,45 @@ def per_tensor_scale(x) -> np.float32:
     return np.float32(amax / np.float32(E4M3_MAX))
 
 
-def quantize_e4m3_sat(x, scale) -> np.ndarray:
+def _quantize_chunk(t: np.ndarray) -> np.ndarray:
+    """Codes of fp32 quotients t: clamp |t| to 448 (saturation), then the nearest value of the
+    non-negative grid, ties to the even code; NaN -> 0x7F; the sign bit is copied."""
+    a = np.minimum(np.abs(t), np.float32(E4M3_MAX)).astype(np.float64)  # NaN stays NaN
+    hi = np.searchsorted(_POS, a, side="left")          # _POS[hi-1] < a <= _POS[hi]
+    np.minimum(hi, len(_POS) - 1, out=hi)               # only NaN lands past the end
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS[lo]
+    d_hi = _POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))   # exact hit: d_hi == 0
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code[np.isnan(t)] = 0x7F
+    return code | (np.signbit(t).astype(np.uint8) << 7)
+
+
+def quantize_e4m3_sat(x, scale, threads: int = 0) -> np.ndarray:
     """Saturating round-to-nearest-even encode of ``float32(x) / float32(scale)``.
 
-    The nearest value is found by searching the table of non-negative finite
-    codes; distances are exact in float64 because both neighbours lie within a
-    factor of two of the input (or the lower one is 0).
+    The nearest value is found by searching the table of non-negative finite codes;
+    distances are exact in float64 because both neighbours lie within a factor of two of
+    the input (or the lower one is 0).  Large inputs are processed in independent chunks,
+    on ``threads`` worker threads if given (elementwise, so the result does not depend on
+    the chunking).
     """
     with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
         t = np.asarray(np.asarray(x, dtype=np.float32) / np.float32(scale), dtype=np.float32)
-    sign = np.signbit(t).astype(np.uint8) << 7
-    a = np.abs(t).astype(np.float64)
-    out = np.zeros(t.shape, dtype=np.uint8)
+    flat = t.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 22
+    spans = [(i, min(i + step, flat.size)) for i in range(0, flat.size, step)]
 
-    nan = np.isnan(t)
-    sat = ~nan & (a >= E4M3_MAX)
-    mid = ~nan & ~sat
-    am = a[mid]
-    hi = np.searchsorted(_POS, am, side="left")        # _POS[hi-1] < am <= _POS[hi]
-    exact = _POS[hi] == am
-    lo = np.maximum(hi - 1, 0)
-    d_lo = am - _POS[lo]
-    d_hi = _POS[hi] - am
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
-    code = np.where(exact | pick_hi, hi, lo).astype(np.uint8)
+    def run(span):
+        out[span[0]:span[1]] = _quantize_chunk(flat[span[0]:span[1]])
 
-    out[mid] = code
-    out[sat] = 0x7E
-    out[nan] = 0x7F
-    return out | sign
+    if threads and threads > 1 and len(spans) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, spans))
+    else:
+        for sp in spans:
+            run(sp)
+    return out.reshape(t.shape)

@@ -14,6 +14,12 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs a real MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long CPU-only checks, opt in with MLA_SLOW=1")
+    # Oracle worker processes fork from a server started here, before any test touches the
+    # GPU, so no process with an initialised GPU runtime ever forks or execs.
+    import multiprocessing as mp
+    import multiprocessing.forkserver as fs
+    mp.set_forkserver_preload(["numpy", "oracle", "synthetic", "tests.oracle_side"])
+    fs.ensure_running()
 
 
 def pytest_collection_modifyitems(config, items):

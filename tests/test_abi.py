@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: exports, argument validation, planner (CPU only).
+
+Every argument check in libmla.so runs before any HIP call, so invalid calls are rejected
+here with fake (never dereferenced) device pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+LIB = os.path.join(ROOT, "fp8_mla_split_amd", "libmla.so")
+HDR = os.path.join(ROOT, "include", "mla.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x1000)  # non-null, never dereferenced by a rejected call
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmla.so is not built (python -m fp8_mla_split_amd.build)")
+    L = ctypes.CDLL(LIB)
+    L.mla_status_string.restype = ctypes.c_char_p
+    L.mla_quantize_fp8_sat.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_float, ctypes.c_void_p]
+    i, f, v, i64 = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64
+    L.mla_decode_splitkv.argtypes = [v, v, v, v, i, i, i, i, i, i, f, f, f, i, i, v, v, i64, v]
+    L.mla_splitkv_combine.argtypes = [v, v, i, i, i, i, v, v, v]
+    L.mla_splitkv_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                   ctypes.POINTER(i64)]
+    return L
+
+
+def header_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ("mla_quantize_fp8_sat", "mla_decode_splitkv", "mla_splitkv_combine",
+              "mla_splitkv_plan", "mla_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in header_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, name in [(0, b"MLA_OK"), (1, b"MLA_ERR_INVALID_ARG"), (2, b"MLA_ERR_UNSUPPORTED"),
+                       (3, b"MLA_ERR_WORKSPACE"), (4, b"MLA_ERR_HIP"), (99, b"MLA_ERR_UNKNOWN")]:
+        assert lib.mla_status_string(code) == name
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    q = lib.mla_quantize_fp8_sat
+    assert q(FAKE, FAKE, -1, 1.0, None) == INVALID
+    assert q(FAKE, FAKE, 10, float("nan"), None) == INVALID
+    assert q(FAKE, FAKE, 10, float("inf"), None) == INVALID
+    assert q(FAKE, FAKE, 10, 0.0, None) == INVALID
+    assert q(FAKE, FAKE, 10, -2.0, None) == INVALID
+    assert q(None, FAKE, 10, 1.0, None) == INVALID
+    assert q(FAKE, None, 10, 1.0, None) == INVALID
+    assert q(None, None, 0, 1.0, None) == OK          # empty: nothing enqueued
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, kv=FAKE, pt=FAKE, sl=FAKE, B=1, Sq=1, H=16, P=64, maxp=4, maxl=256,
+             qs=1.0, ks=1.0, sm=0.07, S=4, r=32, po=FAKE, pl=FAKE, cap=1 << 20)
+    a.update(kw)
+    return lib.mla_decode_splitkv(a["q"], a["kv"], a["pt"], a["sl"], a["B"], a["Sq"], a["H"],
+                                  a["P"], a["maxp"], a["maxl"], a["qs"], a["ks"], a["sm"],
+                                  a["S"], a["r"], a["po"], a["pl"], a["cap"], None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, q=None) == INVALID
+    assert _decode(lib, kv=None) == INVALID
+    assert _decode(lib, pt=None) == INVALID
+    assert _decode(lib, sl=None) == INVALID
+    assert _decode(lib, po=None) == INVALID
+    assert _decode(lib, pl=None) == INVALID
+    assert _decode(lib, B=-1) == INVALID
+    assert _decode(lib, Sq=0) == INVALID
+    assert _decode(lib, H=0) == INVALID
+    assert _decode(lib, maxp=0) == INVALID
+    assert _decode(lib, S=-1) == INVALID
+    assert _decode(lib, qs=float("nan")) == INVALID
+    assert _decode(lib, ks=0.0) == INVALID
+    assert _decode(lib, sm=float("inf")) == INVALID
+    assert _decode(lib, cap=-1) == INVALID
+    assert _decode(lib, S=0, maxl=0) == INVALID        # planner needs a length bound
+
+
+def test_decode_unsupported_shapes_and_workspace(lib):
+    assert _decode(lib, P=48) == UNSUPPORTED            # pages must hold whole 32-token tiles
+    assert _decode(lib, P=16) == UNSUPPORTED
+    assert _decode(lib, Sq=2, H=40000) == UNSUPPORTED   # more than 65536 rows
+    assert _decode(lib, r=48) == UNSUPPORTED
+    assert _decode(lib, S=70000) == UNSUPPORTED
+    assert _decode(lib, cap=4 * 16 - 1) == WORKSPACE    # B*S*Sq*H = 64 entries needed
+    assert _decode(lib, B=0, q=None, kv=None) == OK     # empty batch: nothing enqueued
+
+
+def test_combine_rejects_bad_arguments(lib):
+    c = lib.mla_splitkv_combine
+    assert c(None, FAKE, 1, 4, 1, 16, FAKE, None, None) == INVALID
+    assert c(FAKE, None, 1, 4, 1, 16, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, None, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 0, 1, 16, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, -1, 4, 1, 16, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 5000, 1, 16, FAKE, None, None) == UNSUPPORTED
+    assert c(None, None, 0, 4, 1, 16, None, None, None) == OK
+
+
+def _plan(lib, B, Sq, H, L, cu):
+    s, r, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    st = lib.mla_splitkv_plan(B, Sq, H, L, cu, ctypes.byref(s), ctypes.byref(r), ctypes.byref(n))
+    return st, s.value, r.value, n.value
+
+
+def test_plan_rejects_bad_arguments(lib):
+    assert _plan(lib, 0, 1, 128, 1000, 256)[0] == INVALID
+    assert _plan(lib, 1, 1, 128, 0, 256)[0] == INVALID
+    assert _plan(lib, 1, 1, 128, 1000, -1)[0] == INVALID
+    assert _plan(lib, 1, 2, 40000, 1000, 256)[0] == UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,Sq,H,L", [(1, 1, 128, 131072), (16, 1, 128, 131072),
+                                      (32, 1, 128, 131072), (4, 8, 128, 1048576),
+                                      (1, 1, 16, 256), (3, 2, 48, 5000)])
+def test_plan_fills_the_machine_and_is_consistent(lib, B, Sq, H, L):
+    st, S, r, n = _plan(lib, B, Sq, H, L, 256)
+    assert st == OK and S >= 1 and r in (32, 64, 128)
+    assert n == B * S * Sq * H
+    G = -(-(Sq * H) // r)
+    tiles = -(-L // 32)
+    assert S <= max(1, tiles)                     # no more chunks than tiles
+    if tiles >= 4 * 256:                          # long contexts: enough workgroups for 256 CUs
+        assert B * S * G >= 256
+
+
+def test_split_count_follows_cu_count_and_context(lib):
+    """The split count is derived from the machine and the shape, not a constant."""
+    s_256 = _plan(lib, 1, 1, 128, 131072, 256)[1]
+    s_128 = _plan(lib, 1, 1, 128, 131072, 128)[1]
+    s_short = _plan(lib, 1, 1, 128, 4096, 256)[1]
+    assert s_128 < s_256
+    assert s_short < s_256
+    assert _plan(lib, 64, 1, 128, 131072, 256)[1] < s_256

@@ -1,0 +1,36 @@
+"""GPU LSE combine in isolation on oracle-made partials (runs on an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import fp8_mla_split_amd as mla
+from oracle import combine_fp64
+from tests.oracle_side import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,S,Sq,H", [(1, 1, 1, 16), (2, 3, 2, 16), (1, 64, 1, 128),
+                                      (3, 100, 1, 32), (1, 17, 8, 16)])
+def test_combine_matches_oracle(B, S, Sq, H):
+    rng = np.random.default_rng(S * 7 + H)
+    R = Sq * H
+    po = rng.standard_normal((B, S, R, 512)).astype(np.float32)
+    pl = (rng.standard_normal((B, S, R)) * 4).astype(np.float32)
+    if S > 1:
+        pl[:, ::3, :] = -np.inf                      # empty splits ...
+        po[:, ::3, :, :] = np.nan                    # ... whose partial values are garbage
+    pl[0, :, 0] = -np.inf                            # a row with nothing visible
+    o_ref, l_ref = combine_fp64(np.where(np.isnan(po), 0, po).astype(np.float64),
+                                pl.astype(np.float64))
+    out, lse = mla.splitkv_combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                                   Sq, H)
+    o = bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)).reshape(B, R, 512)
+    o_ref = o_ref.reshape(B, R, 512)
+    # bf16 rounding of the exact merge plus fp32 accumulation
+    assert np.all(np.abs(o - o_ref) <= np.abs(o_ref) * 2.0 ** -8 + 1e-6)
+    assert np.all(o[0, 0] == 0)
+    lse = lse.cpu().numpy().reshape(B, R)
+    fin = np.isfinite(l_ref.reshape(B, R))
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.max(np.abs(lse[fin] - l_ref.reshape(B, R)[fin])) <= 1e-5

@@ -1,0 +1,175 @@
+"""GPU split-KV decode + combine vs the fp64 oracle (runs on an MI355X).
+
+Small cases cover several tiles, ragged tails, causal multi-token queries, paged pools with
+NaN-poisoned page tails, row counts that do not fill a workgroup, and every row-group size.
+The full-size workloads are checked on sampled requests and heads, in the launch
+configuration the benchmark uses (planner's choice, plus the fixed 64-way split).
+"""
+import math
+import zlib
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_mla_split_amd as mla
+from fp8_mla_split_amd.workload import materialize
+from oracle import quantize_e4m3_sat
+from synthetic import WORKLOADS, Workload
+from tests import oracle_side as ors
+
+pytestmark = pytest.mark.gpu
+
+SM = 1.0 / math.sqrt(192.0)
+
+
+def _bf16(t: torch.Tensor) -> np.ndarray:
+    return ors.bf16_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def _run(dw, num_splits=0, rows_per_group=0):
+    po, pl, S = mla.decode_splitkv(dw.q8, dw.kv_pool8, dw.page_table, dw.seq_lens, dw.q_scale,
+                                   dw.kv_scale, dw.w.softmax_scale, dw.max_seq_len,
+                                   num_splits, rows_per_group)
+    out, lse = mla.splitkv_combine(po, pl, dw.w.q_tokens, dw.w.heads)
+    torch.cuda.synchronize()
+    return _bf16(out), lse.cpu().numpy(), S
+
+
+def _oracle(dw, requests, heads=None):
+    w = dw.w
+    q_scale, kv_scale = ors.scales(w, dw.seq_lens_host)
+    assert np.float32(dw.q_scale) == q_scale and np.float32(dw.kv_scale) == kv_scale
+    res = {}
+    for b in requests:
+        L = int(dw.seq_lens_host[b])
+        kv8 = ors.kv8_request(w, b, L, kv_scale)
+        q8 = ors.q8_request(w, b, q_scale)
+        res[b] = ors.attention_request(w, b, L, q8, q_scale, kv8, kv_scale, heads)
+    return res
+
+
+def _compare(dw, got_o, got_l, ref, heads=None):
+    stats = []
+    for b, (o_ref, l_ref) in ref.items():
+        go = got_o[b] if heads is None else got_o[b][:, heads]
+        gl = got_l[b] if heads is None else got_l[b][:, heads]
+        stats.append(ors.check_output(go, o_ref, gl, l_ref))
+    return stats
+
+
+# ------------------------------------------------------------------ small cases
+
+SMALL = [
+    # name, B, H, Sq, lens, page_size, permuted, splits, rows_per_group
+    ("one_token", 1, 16, 1, [1], 0, False, 1, 32),
+    ("ragged_tail", 2, 16, 1, [33, 95], 0, False, 2, 32),
+    ("several_tiles_h48", 1, 48, 1, [1000], 0, False, 3, 64),
+    ("causal_sq2", 2, 16, 2, [2, 70], 0, False, 1, 32),
+    ("causal_sq8_paged", 3, 32, 8, [8, 300, 129], 64, True, 4, 64),
+    ("paged_p32", 4, 64, 1, [31, 64, 65, 2049], 32, True, 5, 32),
+    ("rows_128", 1, 128, 1, [4500], 0, False, 8, 128),
+    ("h256_rows64", 2, 256, 1, [700, 1300], 64, True, 3, 64),
+    ("more_splits_than_tiles", 1, 16, 1, [100], 0, False, 16, 32),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_cases_match_oracle(case):
+    name, B, H, Sq, lens, P, perm, S, r = case
+    w = Workload(name, batch=B, heads=H, q_tokens=Sq, context=None, context_range=(1, 1),
+                 page_size=P, permuted_pool=perm, seed=zlib.crc32(name.encode()) % 1000)
+    dw = materialize(w, seq_lens=np.array(lens, np.int32))
+    o, l, _ = _run(dw, S, r)
+    ref = _oracle(dw, range(B))
+    _compare(dw, o, l, ref)
+
+
+def test_empty_request_and_short_context():
+    w = Workload("edge", batch=3, heads=16, q_tokens=4, context=None, context_range=(1, 1),
+                 page_size=64, permuted_pool=True, seed=5)
+    dw = materialize(w, seq_lens=np.array([0, 2, 80], np.int32))
+    o, l, _ = _run(dw, 3, 32)
+    assert np.all(o[0] == 0) and np.all(l[0] == -np.inf)       # nothing to attend to
+    # L = 2 < Sq = 4: query tokens 0 and 1 see nothing, tokens 2 and 3 see 1 and 2 positions
+    assert np.all(o[1][:2] == 0) and np.all(l[1][:2] == -np.inf)
+    ref = _oracle(dw, [1, 2])
+    ors.check_output(o[1][2:], ref[1][0][2:], l[1][2:], ref[1][1][2:])
+    ors.check_output(o[2], ref[2][0], l[2], ref[2][1])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = Workload("det", batch=2, heads=64, q_tokens=1, context=3000, page_size=64,
+                 permuted_pool=True, seed=3)
+    dw = materialize(w)
+    a = _run(dw, 7, 32)
+    b = _run(dw, 7, 32)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_split_count_does_not_change_the_answer():
+    w = Workload("splits", batch=1, heads=32, q_tokens=1, context=8192, seed=4)
+    dw = materialize(w)
+    ref = _oracle(dw, [0])
+    outs = []
+    for S, r in [(1, 32), (2, 64), (7, 32), (64, 32), (256, 32)]:
+        o, l, _ = _run(dw, S, r)
+        _compare(dw, o, l, ref)
+        outs.append(o)
+    # different partitions of the same sum agree far inside the contract
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 2e-3
+
+
+# ------------------------------------------------------------- full workloads
+
+@pytest.fixture(scope="module")
+def full():
+    cache = {}
+
+    def get(key):
+        if key not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[key] = materialize(WORKLOADS[key])
+        return cache[key]
+
+    yield get
+    cache.clear()
+    torch.cuda.empty_cache()
+
+
+def test_tiny_workload(full):
+    dw = full("tiny")
+    o, l, S = _run(dw, 4, 0)
+    assert S == 4
+    _compare(dw, o, l, _oracle(dw, [0]))
+
+
+@pytest.mark.parametrize("splits", [64, 0])
+def test_b1_128k(full, splits):
+    dw = full("b1_128k")
+    o, l, S = _run(dw, splits, 0)
+    _compare(dw, o, l, _oracle(dw, [0]))
+
+
+def test_b16_128k_sampled(full):
+    dw = full("b16_128k")
+    o, l, _ = _run(dw)
+    _compare(dw, o, l, _oracle(dw, [0, 9, 15]))
+
+
+def test_paged_b32_sampled(full):
+    dw = full("paged_b32")
+    o, l, _ = _run(dw)
+    lens = dw.seq_lens_host
+    picks = [int(np.argmin(lens)), int(np.argmax(lens)), 13]
+    _compare(dw, o, l, _oracle(dw, picks))
+
+
+def test_verify_b4_1m_sampled(full):
+    dw = full("verify_b4_1m")
+    o, l, _ = _run(dw)
+    heads = [0, 77, 127]
+    _compare(dw, o, l, _oracle(dw, [0, 3], heads=heads), heads=heads)

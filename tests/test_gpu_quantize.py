@@ -1,0 +1,93 @@
+"""GPU saturating quantiser vs the oracle: bit-exact (runs on an MI355X)."""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_mla_split_amd as mla
+from oracle import per_tensor_scale, quantize_e4m3_sat
+from synthetic import WORKLOADS, kv_request_f32, q_f32
+from tests import oracle_side
+from tests.test_oracle_e4m3 import _structured_fp32
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_codes(x: np.ndarray, scale) -> np.ndarray:
+    out = mla.quantize_fp8_sat(torch.from_numpy(np.ascontiguousarray(x)).cuda(), float(scale))
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.0123, 3.5e-3, 7.0])
+def test_structured_sweep_bit_exact(scale):
+    x = _structured_fp32()
+    s = np.float32(scale)
+    assert np.array_equal(_gpu_codes(x, s), quantize_e4m3_sat(x, s))
+
+
+def test_unaligned_and_ragged_buffers():
+    x = np.random.default_rng(1).standard_normal(1_000_037).astype(np.float32) * 200
+    t = torch.from_numpy(x).cuda()
+    s = np.float32(0.37)
+    ref = quantize_e4m3_sat(x, s)
+    for lo, hi in [(0, 1_000_037), (1, 999_999), (3, 19), (16, 16 * 4001 + 5), (5, 6)]:
+        out = torch.full((hi - lo + 3,), 0xAA, dtype=torch.uint8, device="cuda")
+        mla.quantize_fp8_sat(t[lo:hi], float(s), out=out[1:1 + hi - lo])
+        got = out.cpu().numpy()
+        assert np.array_equal(got[1:1 + hi - lo], ref[lo:hi]), (lo, hi)
+        assert got[0] == 0xAA and np.all(got[1 + hi - lo:] == 0xAA)   # nothing written outside
+
+
+def _range_hash_oracle(args):
+    start, n = args
+    x = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    return hashlib.sha1(quantize_e4m3_sat(x, 1.0).tobytes()).hexdigest()
+
+
+def test_all_fp32_bit_patterns_bit_exact():
+    """All 2^32 fp32 inputs (scale 1): GPU codes hashed per 2^26-pattern range and compared
+    with the oracle's hashes of the same range."""
+    step = 1 << 26
+    ranges = [(s, step) for s in range(0, 1 << 32, step)]
+    ref = oracle_side._map(_range_hash_oracle, ranges)
+    got = []
+    for start, n in ranges:
+        bits = torch.arange(start, start + n, dtype=torch.int64, device="cuda")
+        x = bits.to(torch.int32).view(torch.float32) if start < (1 << 31) else \
+            (bits - (1 << 32)).to(torch.int32).view(torch.float32)
+        codes = mla.quantize_fp8_sat(x, 1.0).cpu().numpy()
+        got.append(hashlib.sha1(codes.tobytes()).hexdigest())
+    bad = [hex(r[0]) for r, a, b in zip(ranges, got, ref) if a != b]
+    assert not bad, bad
+
+
+def test_tiny_workload_q_and_kv_bit_exact():
+    w = WORKLOADS["tiny"]
+    q = q_f32(w)
+    kv = kv_request_f32(w, 0, 256)
+    for x in (q, kv):
+        s = per_tensor_scale(x)
+        assert np.array_equal(_gpu_codes(x, s), quantize_e4m3_sat(x, s))
+
+
+def test_128k_kv_bit_exact():
+    w = WORKLOADS["b1_128k"]
+    kv = kv_request_f32(w, 0, 131072)
+    s = per_tensor_scale(kv)
+    got = _gpu_codes(kv, s)
+    ref = oracle_side.kv8_request(w, 0, 131072, s)
+    assert np.array_equal(got.reshape(ref.shape), ref)
+
+
+def test_outlier_workload_saturates_to_448_never_nan():
+    w = WORKLOADS["paged_b32"]
+    L = 20000
+    base = kv_request_f32(w, 3, L, with_outliers=False)
+    x = kv_request_f32(w, 3, L, with_outliers=True)
+    s = per_tensor_scale(base)                  # calibrated on the values before injection
+    got = _gpu_codes(x, s)
+    assert np.array_equal(got, quantize_e4m3_sat(x, s))
+    sat = np.mean((got & 0x7F) == 0x7E)
+    assert 0.008 < sat < 0.012, sat             # ~1 % of values are x1000 outliers
+    assert not np.any((got & 0x7F) == 0x7F)     # no NaN codes

@@ -75,7 +75,8 @@ __device__ __forceinline__ int tok_of(int gg, int r) { return 8 * (r >> 2) + 4 *
 
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff,
                                       __amdgpu_buffer_rsrc_t rsrc) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  // one wait state between the M0 write and the LDS DMA that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(rsrc)
                : "memory", "m0");
@@ -194,6 +195,9 @@ void decode_kernel(const DecodeParams p) {
   // ---- DMA of one stage (TL tiles).  Stages past the chunk load nothing (resource with 0
   // records -> zeros) so every wave issues the same count and the vmcnt arithmetic holds.
   const int P = p.page_size;
+  // LDS byte address of the ring (M0 of the DMA takes an LDS address, not a flat pointer)
+  const uint32_t lds_base =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
   // The page table is never written while the kernel runs; reading it through the constant
   // address space lets the compiler use scalar loads, which wait on lgkmcnt and so do not
   // force a vmcnt(0) drain of the in-flight KV DMA.
@@ -223,7 +227,7 @@ void decode_kernel(const DecodeParams p) {
         const uint32_t pch = 64u * k + (uint32_t)lane_v;  // 16-B chunk index in the slot
         const uint32_t row = (pch * 1772u) >> 16;         // pch / 37 for pch < 1216
         const uint32_t voff = 16u * (pch - row);          // row * 576 + col * 16
-        dma16((uint32_t)(slot * kSlot + k * 1024), voff, rsrc);
+        dma16(lds_base + (uint32_t)(slot * kSlot + k * 1024), voff, rsrc);
       }
     }
   };

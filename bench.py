@@ -38,7 +38,23 @@ def _parse():
     ap.add_argument("--rows-per-group", type=int, default=0, help="0 = planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, --steps times (the "
+                         "reference kernel that calibrates HBM byte counters), then exit")
     return ap.parse_args()
+
+
+def copy_probe(mib, steps):
+    """A plain device-to-device copy of known size: each launch reads and writes exactly
+    mib MiB, which is what the profiler's FETCH_SIZE / WRITE_SIZE should report for it."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": steps}), flush=True)
 
 
 def run_workload(key, steps, warmup, splits, rows_per_group, min_bytes=512 << 20):
@@ -165,6 +181,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if a.copy_probe_mib:
+        copy_probe(a.copy_probe_mib, a.steps)
+        return
     t_wall = time.time()
     main_res = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group)
     print(f"[bench] {a.workload}: {main_res['us_per_step']:.2f} us/step "

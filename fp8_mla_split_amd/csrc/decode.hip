@@ -9,41 +9,50 @@
 // partial results a second kernel merges.  Their stage counts are tuned for a 227/327 KiB
 // shared-memory part with 212 SMs; the layout below is designed for gfx950 instead.
 //
-// Work decomposition.  A workgroup is four wavefronts, one per SIMD (the 512-register budget
-// of a lone wave holds the 32x512 fp32 output accumulator in AGPRs).  It owns 32*RG query
-// rows (rows = (query token, head) pairs of one request) and one chunk of that request's
-// tokens.  Wave w works on row block w / TL and takes every TL-th tile of the chunk
-// (TL = 4 / RG), so with RG = 1 the four waves stream four different tiles and share nothing
-// but the LDS ring; their partial (max, sum, O) are merged in LDS at the end.
+// Work decomposition.  A workgroup is four wavefronts, one per SIMD (a lone wave's 512
+// registers hold a 32x512 fp32 output accumulator in AGPRs).  It owns 32*RG query rows
+// (rows = (query token, head) pairs of one request; RG = 2 or 4) and one chunk of that
+// request's tokens.  Wave w works on row block w / TL and takes every TL-th tile of the chunk
+// (TL = 4 / RG): with RG = 4 all four waves read every tile, with RG = 2 two pairs of waves
+// take alternate tiles.  Waves that share a row block merge (max, sum, O) in LDS at the end.
 //
 // KV staging.  A tile is 32 tokens x 576 bytes.  Tiles go HBM -> LDS with buffer_load ... lds
-// (16 bytes per lane, no VGPR round trip) into an 8-slot ring (151 KiB of the CU's 160 KiB):
-// 8 / TL stages of TL tiles, so 8/TL - 1 stages are in flight while one is consumed.  Rows
-// are stored with a 592-byte pitch (37 x 16 B); the 64-bank LDS then serves both read
-// patterns below without conflicts.  The buffer resource of each tile is bounded by the
-// number of valid rows, so rows past the end of the sequence arrive as zeros: no NaN bytes
-// from a page's unused tail can reach the P.V product (0 x NaN).  The DMA is issued with
-// inline asm and waited on with explicit vmcnt counts because the compiler, when it sees the
-// intrinsic, waits for every outstanding LDS DMA before any LDS read and so removes the
-// pipelining this staging exists for.
+// (16 bytes per lane, no VGPR round trip) into an 8-slot ring (152 KiB of the CU's 160 KiB),
+// grouped in stages of TL tiles.  While the waves work on stages st and st + 1, stages up to
+// st + NST - 1 are in flight (6 tiles for RG = 4, 4 for RG = 2).  Rows are stored with a
+// 592-byte pitch (37 x 16 B); the 64-bank LDS then serves both read patterns below without
+// conflicts.  The buffer resource of each tile is bounded by the number of valid rows, so
+// rows past the end of the sequence arrive as zeros: no NaN bytes from a page's unused tail
+// can reach the P.V product (0 x NaN).  The query rows are staged through the same ring (in
+// its last RG slots, before the ring starts) and then held in registers.  Every DMA is issued
+// from inline asm and waited on with explicit vmcnt counts: the compiler does not track them,
+// so none of its own waits drain the ring, and the kernel issues no compiler-visible global
+// load before the main loop for the same reason.
 //
 // Math per tile (per wave, 32 rows x 32 tokens), all on FP8 MFMA v_mfma_scale_f32_32x32x64:
-//  * S^T = K . Q^T: tokens along M, rows along N, 576 = 9 x 64 channels along K.  Q stays in
-//    registers for the whole kernel.  Computing the transpose puts each lane's 16 scores for
-//    one row exactly where the P.V step needs them as its A operand (no data movement).
-//    MFMA token m reads LDS row perm_row(m); the permutation makes the transposed V reads
-//    below touch 8 rows of one parity, which is what keeps them conflict-free.
+//  * S^T = K . Q^T: tokens along M, rows along N, 576 = 9 x 64 channels along K.  Computing
+//    the transpose puts each lane's 16 scores for one row exactly where the P.V step needs
+//    them as its A operand (no data movement).  MFMA token m reads LDS row perm_row(m); the
+//    permutation makes the transposed V reads below touch 8 rows of one parity, which keeps
+//    them conflict-free.
 //  * Online softmax in base 2 against a fixed reference max mu per row (the max of the row's
 //    first tile with a visible position), so the 256-register O is never rescaled.  Each
-//    tile's probabilities are instead normalised per row by 2^-e (e = floor of the tile max
+//    tile's probabilities are normalised per row by 2^-e (e = floor of the row's tile max
 //    above mu) before the FP8 cast, and the MFMA's per-lane E8M0 scale multiplies them back
-//    by 2^e.  If a row's true max ends up more than kHeadroom above mu (fp32 range at
-//    risk), the workgroup recomputes its chunk once with mu = the true max.
+//    by 2^e.  The two lanes that hold a row (n and n + 32) must use the same e: each holds
+//    16 K-elements of both 32-element scale blocks of the row, and a block's scale is read
+//    from one of them.  If a row's true max ends up more than kHeadroom above mu (fp32 range
+//    at risk), the workgroup recomputes its chunk once with mu = the true max.
 //  * P is encoded as hi = e4m3(p) and lo = e4m3(p - hi), both in the same units; one
 //    32x32x64 MFMA takes [hi | lo] for 32 tokens against [V | V], i.e. P.V with about
 //    7 bits of P mantissa.  (A single e4m3 P costs ~3e-3 normalised L1 error against the
 //    fp64 oracle at 128K context, more than the 2e-3 budget.)
 //  * V (the first 512 columns of the same tile) is read transposed with ds_read_b64_tr_b8.
+//  * Software pipeline: the 9 QK MFMAs of tile i+1 are issued before the 16 PV MFMAs of tile
+//    i, and the softmax of tile i+1 (about 100 VALU instructions per lane) is issued in the
+//    gaps between those PV MFMAs, so the matrix pipe is not left idle while the VALU works.
+#include <type_traits>
+
 #include "internal.h"
 
 namespace mla {
@@ -73,24 +82,35 @@ __device__ __forceinline__ int perm_row(int m) {
 // Token index held in register r of a 32x32 MFMA result by lanes of half gg.
 __device__ __forceinline__ int tok_of(int gg, int r) { return 8 * (r >> 2) + 4 * gg + (r & 3); }
 
+// 16 bytes per lane, global -> LDS at M0 + 16 * lane, with M0 = lds_addr + IMM (the
+// constant part of the address stays out of the register file).  One wait state separates
+// the M0 write from the DMA that reads it.
+template <int IMM>
 __device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff,
                                       __amdgpu_buffer_rsrc_t rsrc) {
-  // one wait state between the M0 write and the LDS DMA that reads it
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "n"(IMM)
+               : "memory", "m0", "scc");
 }
 
-// FP8 x FP8 32x32x64 MFMA with explicit register classes.  The compiler, left to itself,
-// puts every MFMA accumulator of this kernel into AGPRs; the 16 score registers then evict
-// part of the 256-register O accumulator and Q gets spilled.  Issuing the instruction from
-// asm pins the scores to VGPRs and O to AGPRs.  The "memory" clobber keeps the LDS
-// fragment reads where the source places them (one MFMA ahead), which bounds how many
-// fragment registers are live at once.  Hazards the compiler cannot see through the
-// asm are covered explicitly: s_nop 1 before each MFMA covers a VALU write of an operand
-// just before it, and mfma_drain() (24 wait states, more than the 16-pass instruction's
-// requirement) separates the last MFMA of a chain from any non-MFMA reader of its result.
+// As dma16, for the unrolled Q staging loop whose offsets are compile-time after unrolling.
+__device__ __forceinline__ void dma16_q(uint32_t lds_addr, uint32_t voff,
+                                        __amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
+  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(off)
+               : "memory", "m0", "scc");
+}
+
+// FP8 x FP8 32x32x64 MFMA with explicit register classes: the scores live in VGPRs and O in
+// AGPRs (left to itself the compiler puts every accumulator in AGPRs, which then do not
+// hold O).  The "memory" clobber keeps the LDS fragment reads where the source places them.
+// Hazards the compiler cannot see through the asm are covered explicitly: s_nop 1 before
+// each MFMA covers a VALU write of an operand just before it, and at least 24 wait states
+// separate the last MFMA of a chain from any non-MFMA reader of its result (mfma_drain,
+// which takes the accumulator as an operand: the compiler treats an asm output as ready
+// at once and would otherwise copy it straight after the MFMA).
 __device__ __forceinline__ f32x16 mfma_qk_first(const i32x8& a, const i32x8& b) {
   f32x16 d;
   asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
@@ -111,16 +131,41 @@ __device__ __forceinline__ void mfma_pv(f32x16& acc, const i32x8& a, const i32x8
                : "v"(a), "v"(b), "v"(scale_a), "v"(127)
                : "memory");
 }
-__device__ __forceinline__ void mfma_drain() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+// 24 wait states after the last MFMA that wrote acc, before anything reads it.  acc is an
+// operand so that no read or copy of it can be placed ahead of the wait states.
+__device__ __forceinline__ void mfma_drain(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc)::"memory");
 }
+__device__ __forceinline__ void mfma_drain_acc(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc)::"memory");
+}
+// Orders later reads of acc after the preceding asm (no wait states of its own).
+__device__ __forceinline__ void acc_fence(f32x16& acc) { asm volatile("" : "+a"(acc)); }
+// (value of lane n, value of lane n + 32) in every lane n and n + 32, by one
+// v_permlane32_swap (no LDS traffic).
+__device__ __forceinline__ f32x2 row_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return (f32x2){__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// One accumulator block, copied to VGPRs where it is used.  The empty asm keeps the compiler
+// from hoisting the copies of all 256 accumulator registers to one place, which would need
+// more VGPRs than a wave has.
+__device__ __forceinline__ f32x16 from_acc(const f32x16& a) {
+  f32x16 v;
+  asm volatile("" : "=v"(v) : "0"(a));
+  return v;
+}
+// Keeps the compiler from moving instructions across this point (used to interleave the
+// softmax VALU work with the PV MFMAs in source order).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-
 __device__ __forceinline__ i32x4 lds_read16(const uint8_t* lds, uint32_t addr) {
   return *(const i32x4*)(lds + addr);
 }
@@ -130,19 +175,42 @@ __device__ __forceinline__ i32x2 lds_read_tr8(uint8_t* lds, uint32_t addr) {
       (__attribute__((address_space(3))) i32x2*)(lds + addr));
 }
 
+// Softmax state of one lane: its row's reference max, the running true max and its share of
+// the row's sum of 2^(x - mu) * 224.
+struct RowState {
+  float mu, m_true, l_run;
+};
+
+// One tile's probabilities, in pieces that the caller interleaves with MFMAs.
+struct SoftmaxTile {
+  f32x16 s;   // raw scores
+  float off;  // exp2 argument offset
+  float psum;
+  int ef;
+  float pv[16];
+  i32x8 pa;
+};
+
 template <int RG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const DecodeParams p) {
-  constexpr int TL = 4 / RG;               // tile lanes (waves sharing a row block)
-  constexpr int NST = kSlots / TL;         // ring stages
-  constexpr int LOADS = (TL * kDmaPerTile) / 4;  // DMA instructions per wave per stage (min)
-  constexpr int VMC = (NST - 2) * LOADS;
+  constexpr int TL = 4 / RG;               // waves sharing a row block
+  constexpr int NST = kSlots / TL;         // stages in the ring
+  constexpr int LMIN = 4 * TL;             // fewest DMA instructions a wave issues per stage
+  constexpr int QSLOT = kSlots - RG;       // the query rows are staged in the last RG slots
+  constexpr int P0 = QSLOT / TL;           // stages that fit beside them
+  constexpr int QDMA = 18 * RG;            // 32*RG rows x 576 B / 1 KiB per DMA instruction
+  static_assert(RG == 2 || RG == 4, "row blocks per workgroup");
+  static_assert(NST >= 4 && P0 >= 1 && P0 <= NST - 1, "ring layout");
+  static_assert(32 * RG * kD <= RG * kSlot, "staged Q fits its slots");
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  const uint32_t lds_base =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int rg = wave / TL, tl = wave % TL;
+  const int rb = wave / TL, tl = wave % TL;
   const int n = lane & 31, gg = lane >> 5;
 
   // ---- workgroup -> (request, split, row group); the G row groups of one split share an
@@ -155,7 +223,12 @@ void decode_kernel(const DecodeParams p) {
   if (u >= p.batch * S) return;
   const int b = u / S, s = u - b * S;
 
-  int L = p.seq_lens[b];
+  // Wave-uniform scalars come from the constant address space (scalar loads, lgkmcnt).
+  const __attribute__((address_space(4))) int32_t* seq_lens =
+      (const __attribute__((address_space(4))) int32_t*)p.seq_lens;
+  const __attribute__((address_space(4))) int32_t* page_table =
+      (const __attribute__((address_space(4))) int32_t*)p.page_table;
+  int L = seq_lens[b];
   const int Lmax = p.max_pages * p.page_size;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int ntiles_all = (L + kTile - 1) / kTile;
@@ -171,65 +244,52 @@ void decode_kernel(const DecodeParams p) {
     return;
   }
 
-  const int wrow0 = row0 + rg * 32;
+  const int wrow0 = row0 + rb * 32;
   const int R = wrow0 + n;  // this lane's query row (score and P layout)
   const bool row_ok = R < M;
   // last visible position of the row (bottom-right causal); rows past M are never stored
   const int lim = row_ok ? L - p.q_tokens + R / p.heads : 0x7FFFFFFF;
   const int lim_min = L - p.q_tokens + wrow0 / p.heads;
-
-  // ---- Q fragments (B operand of S^T = K . Q^T), kept for the whole kernel
-  i32x8 qf[9];
-  const uint8_t* qsrc = p.q8 + ((int64_t)b * M + (row_ok ? R : 0)) * kD + 32 * gg;
-  auto load_q = [&]() {
-#pragma unroll
-    for (int c = 0; c < 9; ++c) {
-      const i32x4 lo = *(const i32x4*)(qsrc + 64 * c);
-      const i32x4 hi = *(const i32x4*)(qsrc + 64 * c + 16);
-      qf[c] = row_ok ? (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}
-                     : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  };
-  load_q();
-
-  // ---- DMA of one stage (TL tiles).  Stages past the chunk load nothing (resource with 0
-  // records -> zeros) so every wave issues the same count and the vmcnt arithmetic holds.
+  const int nsteps = (ntiles + TL - 1) / TL;
   const int P = p.page_size;
-  // LDS byte address of the ring (M0 of the DMA takes an LDS address, not a flat pointer)
-  const uint32_t lds_base =
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
-  // The page table is never written while the kernel runs; reading it through the constant
-  // address space lets the compiler use scalar loads, which wait on lgkmcnt and so do not
-  // force a vmcnt(0) drain of the in-flight KV DMA.
-  const __attribute__((address_space(4))) int32_t* page_table =
-      (const __attribute__((address_space(4))) int32_t*)p.page_table;
-  auto issue_stage = [&](int st) {
+
+  // ---- DMA lane offsets.  Of a tile's 19 DMA instructions, wave w issues k = w, w+4, ...
+  // Chunk pch = 64k + lane of the tile is row pch / 37, 16-byte column pch % 37 of the LDS
+  // tile; column 36 is the pad (it receives the next row's first 16 bytes, or zeros).
+  uint32_t voff[5];
 #pragma unroll
-    for (int j = 0; j < TL; ++j) {
-      const int ti = st * TL + j;
-      const int slot = (st % NST) * TL + j;
-      const uint8_t* base = p.kv;
-      int nrec = 0;
-      if (ti < ntiles) {
-        const int T0 = (t_begin + ti) * kTile;
-        const int page = page_table[(int64_t)b * p.max_pages + T0 / P];  // scalar load
-        base = p.kv + ((int64_t)page * P + (T0 % P)) * kD;
-        nrec = min(kTile, L - T0) * kD;
-      }
-      const __amdgpu_buffer_rsrc_t rsrc =
-          __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, 0x00020000);
-      // instruction q = 19 j + k of the stage belongs to wave q % 4.  The lane id is routed
-      // through an opaque move so the per-lane offsets are recomputed here (4 VALU each)
-      // instead of being hoisted out of the tile loop into ~19 permanently live VGPRs.
-      int lane_v;
-      asm volatile("v_mov_b32 %0, %1" : "=v"(lane_v) : "v"(lane));
-      for (int k = ((wave - kDmaPerTile * j) % 4 + 4) % 4; k < kDmaPerTile; k += 4) {
-        const uint32_t pch = 64u * k + (uint32_t)lane_v;  // 16-B chunk index in the slot
-        const uint32_t row = (pch * 1772u) >> 16;         // pch / 37 for pch < 1216
-        const uint32_t voff = 16u * (pch - row);          // row * 576 + col * 16
-        dma16(lds_base + (uint32_t)(slot * kSlot + k * 1024), voff, rsrc);
-      }
+  for (int i = 0; i < 5; ++i) {
+    const uint32_t pch = 64u * (uint32_t)(wave + 4 * i) + (uint32_t)lane;
+    const uint32_t row = pch / 37u;
+    voff[i] = 16u * (pch - row);
+  }
+
+  // this wave's share of a tile: instructions k = wave + 4 i (i < 4, and i = 4 for waves
+  // 0..2), i.e. LDS bytes wave * 1024 + i * 4096 of the slot
+  const uint32_t wave_lds = lds_base + (uint32_t)wave * 1024u;
+  auto issue_tile = [&](int st, uint32_t slot_lds, auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    const int ti = st * TL + j;
+    const uint8_t* base = p.kv;
+    int nrec = 0;
+    if (ti < ntiles) {
+      const int T0 = (t_begin + ti) * kTile;
+      const int page = page_table[(int64_t)b * p.max_pages + T0 / P];
+      base = p.kv + ((int64_t)page * P + (T0 % P)) * kD;
+      nrec = min(kTile, L - T0) * kD;
     }
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, 0x00020000);
+    dma16<j * kSlot + 0 * 4096>(slot_lds, voff[0], rsrc);
+    dma16<j * kSlot + 1 * 4096>(slot_lds, voff[1], rsrc);
+    dma16<j * kSlot + 2 * 4096>(slot_lds, voff[2], rsrc);
+    dma16<j * kSlot + 3 * 4096>(slot_lds, voff[3], rsrc);
+    if (wave < 3) dma16<j * kSlot + 4 * 4096>(slot_lds, voff[4], rsrc);
+  };
+  auto issue_stage = [&](int st) __attribute__((always_inline)) {
+    const uint32_t slot_lds = wave_lds + (uint32_t)((st % NST) * TL * kSlot);
+    issue_tile(st, slot_lds, std::integral_constant<int, 0>{});
+    if constexpr (TL == 2) issue_tile(st, slot_lds, std::integral_constant<int, 1>{});
   };
 
   const int G16 = lane >> 4, i16 = lane & 15;
@@ -237,88 +297,87 @@ void decode_kernel(const DecodeParams p) {
   const uint32_t vrow0 = perm_row(tok_of(gg, i16 >> 1)) * kPitch + vcol;
   const uint32_t vrow1 = perm_row(tok_of(gg, 8 + (i16 >> 1))) * kPitch + vcol;
   const uint32_t krow = perm_row(n) * kPitch + 32 * gg;
-  const int nsteps = (ntiles + TL - 1) / TL;
+  const float c2 = p.c2;
 
-  // ---- per-row softmax state (score layout: lane holds row n; lanes n and n+32 agree).
-  // The reference max mu of a row is the max of its first tile with a visible position; it
-  // never moves during a pass, so the AGPR-resident O is never rescaled.  Each tile's
-  // probabilities are normalised by 2^-e (e = floor(tile max - mu)) before the FP8 cast and
-  // the MFMA multiplies them back by 2^e.  With e <= kHeadroom, O and l stay far below the
-  // fp32 range (O <= 448 * 448 * 2^kHeadroom * tokens).  If some row's true max exceeds its
-  // mu by more than that, the whole workgroup recomputes its chunk once with mu = true max.
-  float mu = -INFINITY;     // reference max (log2 units)
-  float m_true = -INFINITY; // running true max
-  float l_run = 0.f;        // this lane's share of sum 2^(x - mu) * 224
-  f32x16 o[16];
+  auto tile_base = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)(((st % NST) * TL + tl) * kSlot);
+  };
 
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
+  i32x8 qf[9];  // Q fragments (B operand of S^T = K . Q^T), staged once per pass
+
+  // S^T = K . Q^T of this wave's tile of stage st (tokens x rows), one fragment read ahead
+  auto qk = [&](int st) __attribute__((always_inline)) -> f32x16 {
+    const uint32_t tb = tile_base(st) + krow;
+    f32x16 acc;
+    i32x4 a0 = lds_read16(lds, tb);
+    i32x4 a1 = lds_read16(lds, tb + 16);
 #pragma unroll
-    for (int d = 0; d < 16; ++d) o[d] = (f32x16){0.f};
-    l_run = 0.f;
+    for (int c = 0; c < 9; ++c) {
+      const i32x8 a = (i32x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      if (c < 8) {
+        a0 = lds_read16(lds, tb + 64 * (c + 1));
+        a1 = lds_read16(lds, tb + 64 * (c + 1) + 16);
+      }
+      if (c == 0) acc = mfma_qk_first(a, qf[0]);
+      else mfma_qk(acc, a, qf[c]);
+    }
+    return acc;
+  };
+
+  RowState rs{-INFINITY, -INFINITY, 0.f};
+
+  // Softmax of one tile, in 9 pieces that the caller interleaves with MFMAs (piece 0 must
+  // come at least 24 wait states after the last MFMA that wrote t.s).  A tile that this wave
+  // does not own (past the chunk, or past the loop) is masked whole: p = 0, no state change.
+  auto softmax_piece = [&](SoftmaxTile& t, int st, bool valid, int piece)
+      __attribute__((always_inline)) {
+    switch (piece) {
+      case 0: {  // mask the tail / causal positions, lane max, reference max, exponent
+        const int T0 = (t_begin + st * TL + tl) * kTile;
+        if (!valid) {
 #pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
-      if (st < nsteps) issue_stage(st);
-
-    for (int st = 0; st < nsteps; ++st) {
-      if (st + NST - 2 < nsteps) wait_vmcnt<VMC>();
-      else wait_vmcnt<0>();
-      __syncthreads();
-      if (st + NST - 1 < nsteps) issue_stage(st + NST - 1);
-
-      const int ti = st * TL + tl;
-      if (ti >= ntiles) continue;
-      const uint32_t tb = (uint32_t)(((st % NST) * TL + tl) * kSlot);
-
-      // S^T = K . Q^T (tokens x rows), one fragment read ahead of each MFMA
-      f32x16 sacc;
-      i32x4 a0 = lds_read16(lds, tb + krow);
-      i32x4 a1 = lds_read16(lds, tb + krow + 16);
+          for (int r = 0; r < 16; ++r) t.s[r] = -INFINITY;
+        } else if (T0 + kTile - 1 > lim_min) {
+          // register r holds tile token perm_row(tok_of(gg, r)) = 2 r + gg, visible while
+          // T0 + 2 r + gg <= lim, i.e. while r <= c
+          const int c = (lim - T0 - gg) >> 1;
 #pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        const i32x8 a = (i32x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        if (c < 8) {
-          a0 = lds_read16(lds, tb + krow + 64 * (c + 1));
-          a1 = lds_read16(lds, tb + krow + 64 * (c + 1) + 16);
+          for (int r = 0; r < 16; ++r)
+            if (r > c) t.s[r] = -INFINITY;
         }
-        if (c == 0) sacc = mfma_qk_first(a, qf[0]);
-        else mfma_qk(sacc, a, qf[c]);
+        float m = fmaxf(fmaxf(t.s[0], t.s[1]), t.s[2]);
+#pragma unroll
+        for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, t.s[r]), t.s[r + 1]);
+        m = fmaxf(m, t.s[15]);
+        // the row's max over both lanes that hold it (lanes n and n + 32)
+        const f32x2 both = row_pair(m);
+        const float mx = fmaxf(both[0], both[1]) * c2;  // c2 > 0
+        if (rs.mu == -INFINITY) rs.mu = mx;  // first tile with a visible position
+        rs.m_true = fmaxf(rs.m_true, mx);
+        const float mref = rs.mu == -INFINITY ? 0.f : rs.mu;
+        const float ef = fminf(fmaxf(floorf(mx - mref), -126.0f), 127.0f);
+        t.ef = (int)ef;
+        t.off = mref + ef - kLog2PScale;
+        break;
       }
-      mfma_drain();
-
-      float x[16];
+      case 1:
+      case 2:
+      case 3:
+      case 4: {  // p = 2^(c2 s - off), in [0, 448); 0 where masked
+        const int r0 = 4 * (piece - 1);
+        float sum = piece == 1 ? 0.f : t.psum;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = sacc[r] * p.c2;
-      const int T0 = (t_begin + ti) * kTile;
-      if (T0 + kTile - 1 > lim_min) {  // tail or causal tile: mask per element
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (T0 + perm_row(tok_of(gg, r)) > lim) x[r] = -INFINITY;
+        for (int r = r0; r < r0 + 4; ++r) {
+          t.pv[r] = __builtin_amdgcn_exp2f(fmaf(t.s[r], c2, -t.off));
+          sum += t.pv[r];
+        }
+        t.psum = sum;
+        if (piece == 4) rs.l_run += ldexpf(sum, t.ef);
+        break;
       }
-      float mx = x[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (mu == -INFINITY) mu = mx;  // first tile with a visible position (pass 0)
-      m_true = fmaxf(m_true, mx);
-
-      const float mref = mu == -INFINITY ? 0.f : mu;
-      const float ef = fminf(fmaxf(floorf(mx - mref), -126.0f), 127.0f);
-      const float off = mref + ef - kLog2PScale;
-      float pv[16];
-      float lsum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(x[r] - off);  // in [0, 448); 0 where masked
-        lsum += pv[r];
-      }
-      l_run += ldexpf(lsum, (int)ef);
-      const int escale = 127 + (int)ef;
-
-      // P as hi + lo e4m3 bytes: bytes 0..15 of the A operand are hi(p_r), 16..31 lo(p_r)
-      i32x8 pa;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      default: {  // pieces 5..8: P as hi + lo e4m3 bytes (A operand bytes 0..15 hi, 16..31 lo)
+        const int q = piece - 5;
+        const float* pv = t.pv;
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * q], pv[4 * q + 1], 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * q + 2], pv[4 * q + 3], w, true);
         const f32x2 d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
@@ -327,11 +386,78 @@ void decode_kernel(const DecodeParams p) {
                                                  false);
         w2 = __builtin_amdgcn_cvt_pk_fp8_f32(pv[4 * q + 2] - d23[0], pv[4 * q + 3] - d23[1], w2,
                                              true);
-        pa[q] = w;
-        pa[4 + q] = w2;
+        t.pa[q] = w;
+        t.pa[4 + q] = w2;
+        break;
       }
+    }
+  };
 
-      // O += P . V over the 16 blocks of 32 value columns; B = [V | V] for [hi | lo]
+  f32x16 o[16];
+
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) o[d] = (f32x16){0.f};
+    rs.l_run = 0.f;
+    // ---- stage the workgroup's query rows (contiguous in q8) in the last RG slots, with the
+    // first P0 KV stages in flight beside them.  Each pass stages them again, so the Q
+    // fragments are live within a pass only.
+    {
+      const int qrows = min(32 * RG, M - row0);
+      const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.q8 + ((int64_t)b * M + row0) * kD), 0, qrows * kD, 0x00020000);
+      // instruction i = wave + 4 j moves bytes [1024 i, 1024 (i + 1)) of the rows
+      const uint32_t qvoff = (uint32_t)wave * 1024u + 16u * (uint32_t)lane;
+      static_assert(QDMA % 4 == 0, "every wave issues the same number of Q chunks");
+#pragma unroll
+      for (int j = 0; j < QDMA / 4; ++j)
+        dma16_q(wave_lds, qvoff + 4096u * j, qrsrc, QSLOT * kSlot + 4096 * j);
+    }
+    // Every stage is issued, also past the end of the chunk (those load nothing and write
+    // zeros into a free slot), so the number of DMA instructions in flight behind any stage
+    // is fixed and every wait below is a constant.
+#pragma unroll
+    for (int st = 0; st < P0; ++st) issue_stage(st);
+    wait_vmcnt<P0 * LMIN>();  // this wave's Q chunks have landed
+    __syncthreads();
+
+    // Q fragments (B operand of S^T = K . Q^T), in registers for the whole pass
+    {
+      const uint32_t qrow = (uint32_t)(QSLOT * kSlot + (rb * 32 + n) * kD + 32 * gg);
+#pragma unroll
+      for (int c = 0; c < 9; ++c) {
+        const i32x4 lo = lds_read16(lds, qrow + 64 * c);
+        const i32x4 hi = lds_read16(lds, qrow + 64 * c + 16);
+        qf[c] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+    __syncthreads();  // the Q slots are free from here on
+#pragma unroll
+    for (int st = P0; st < NST - 1; ++st) issue_stage(st);
+
+    // first tile: scores and probabilities, not overlapped with anything
+    wait_vmcnt<(NST - 2) * LMIN>();
+    __syncthreads();
+    i32x8 pa;  // P of the tile whose PV comes next, and its per-row exponent
+    int ef;
+    {
+      SoftmaxTile t;
+      t.s = qk(0);
+      mfma_drain(t.s);
+#pragma unroll
+      for (int piece = 0; piece < 9; ++piece) softmax_piece(t, 0, tl < ntiles, piece);
+      pa = t.pa;
+      ef = t.ef;
+    }
+
+    // O += P . V of stage st over the 16 blocks of 32 value columns; B = [V | V] for
+    // [hi | lo].  With a next tile, its softmax fills the gaps between these MFMAs.
+    auto pv_tile = [&](int st, SoftmaxTile& nx, bool next_valid, auto with_next)
+        __attribute__((always_inline)) {
+      constexpr bool kNext = decltype(with_next)::value;
+      const uint32_t tb = tile_base(st);
+      const int escale = 127 + ef;
       i32x2 v0 = lds_read_tr8(lds, tb + vrow0);
       i32x2 v1 = lds_read_tr8(lds, tb + vrow1);
 #pragma unroll
@@ -342,13 +468,39 @@ void decode_kernel(const DecodeParams p) {
           v1 = lds_read_tr8(lds, tb + vrow1 + 32 * (d + 1));
         }
         mfma_pv(o[d], pa, vb, escale);
+        if constexpr (kNext) {
+          sched_fence();
+          if (d == 0) mfma_drain(nx.s);  // the QK chain's result is read from here on
+          if (d < 9) softmax_piece(nx, st + 1, next_valid, d);
+          sched_fence();
+        }
       }
+    };
+
+    for (int st = 0; st + 1 < nsteps; ++st) {
+      wait_vmcnt<(NST - 3) * LMIN>();
+      // stage st + 1 is visible to every wave, and every wave is done with stage st - 1
+      __syncthreads();
+      issue_stage(st + NST - 1);
+      SoftmaxTile t;
+      t.s = qk(st + 1);
+      pv_tile(st, t, (st + 1) * TL + tl < ntiles, std::true_type{});
+      pa = t.pa;
+      ef = t.ef;
     }
-    mfma_drain();
+    {
+      SoftmaxTile unused;
+      pv_tile(nsteps - 1, unused, false, std::false_type{});  // landed before the last barrier
+    }
+    mfma_drain_acc(o[15]);
+#pragma unroll
+    for (int d = 0; d < 15; ++d) acc_fence(o[d]);
+    wait_vmcnt<0>();  // the stages past the chunk have landed too
     // all waves are past their last read of the ring; decide whether to recompute
-    const bool over = mu != -INFINITY && m_true > mu + kHeadroom;
+    const bool over = rs.mu != -INFINITY && rs.m_true > rs.mu + kHeadroom;
     if (!__syncthreads_or(over)) break;
-    mu = m_true;  // second pass: reference = true max, so every e <= 0
+    // second pass: reference = the row's true max, so every exponent is <= 0
+    rs.mu = rs.m_true;
   }
 
   // ---- merge the TL waves of each row block, normalise, write partial O and lse
@@ -356,7 +508,8 @@ void decode_kernel(const DecodeParams p) {
   float* st_m = (float*)lds;        // [4 waves][32]
   float* st_l = st_m + 4 * 32;
   float* st_f = st_l + 4 * 32;
-  const float l_row = l_run + __shfl_xor(l_run, 32);
+  const float mu = rs.mu;
+  const float l_row = rs.l_run + __shfl_xor(rs.l_run, 32);
   if (lane < 32) {
     st_m[wave * 32 + n] = mu;
     st_l[wave * 32 + n] = l_row;
@@ -364,12 +517,12 @@ void decode_kernel(const DecodeParams p) {
   __syncthreads();
   float Mx = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < TL; ++t) Mx = fmaxf(Mx, st_m[(rg * TL + t) * 32 + n]);
+  for (int t = 0; t < TL; ++t) Mx = fmaxf(Mx, st_m[(rb * TL + t) * 32 + n]);
   float Ls = 0.f;
 #pragma unroll
   for (int t = 0; t < TL; ++t) {
-    const float mt = st_m[(rg * TL + t) * 32 + n];
-    if (mt != -INFINITY) Ls += st_l[(rg * TL + t) * 32 + n] * exp2f(mt - Mx);
+    const float mt = st_m[(rb * TL + t) * 32 + n];
+    if (mt != -INFINITY) Ls += st_l[(rb * TL + t) * 32 + n] * exp2f(mt - Mx);
   }
   const float f = (mu != -INFINITY && Ls > 0.f) ? exp2f(mu - Mx) * p.kv_scale / Ls : 0.f;
   if (lane < 32) st_f[wave * 32 + n] = f;
@@ -390,13 +543,22 @@ void decode_kernel(const DecodeParams p) {
 
   float* out = p.partial_o + prow * kDv;
   if constexpr (TL == 1) {
+    // register r of block d is row wrow0 + tok_of(gg, r), column 32 d + n
+    float* wout = out + (int64_t)wrow0 * kDv + n;
+    if (wrow0 + 32 <= M) {
 #pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      const f32x16 v = o[d];
+      for (int d = 0; d < 16; ++d) {
+        const f32x16 v = from_acc(o[d]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wrow0 + tok_of(gg, r);
-        if (row < M) out[(int64_t)row * kDv + 32 * d + n] = v[r] * fr[r];
+        for (int r = 0; r < 16; ++r) wout[tok_of(gg, r) * kDv + 32 * d] = v[r] * fr[r];
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const f32x16 v = from_acc(o[d]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (wrow0 + tok_of(gg, r) < M) wout[tok_of(gg, r) * kDv + 32 * d] = v[r] * fr[r];
       }
     }
   } else {
@@ -407,7 +569,7 @@ void decode_kernel(const DecodeParams p) {
       if (half) __syncthreads();  // previous half fully read
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
-        const f32x16 v = o[8 * half + dd];
+        const f32x16 v = from_acc(o[8 * half + dd]);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           mine[tok_of(gg, r) * kMergeStride + 32 * dd + n] = v[r] * fr[r];
@@ -440,7 +602,6 @@ hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t 
   const int64_t units = (int64_t)p.batch * p.num_splits;
   const int64_t blocks = ((units + 7) / 8) * 8 * p.groups;
   switch (rows_per_group) {
-    case 32: decode_kernel<1><<<(unsigned)blocks, 256, 0, s>>>(p); break;
     case 64: decode_kernel<2><<<(unsigned)blocks, 256, 0, s>>>(p); break;
     case 128: decode_kernel<4><<<(unsigned)blocks, 256, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;

@@ -60,7 +60,7 @@ mla_status plan(int batch, int q_tokens, int heads, int max_seq_len, int cu, int
   const int64_t tiles = cdiv(max_seq_len, 32);
   double best = -1.0;
   int best_s = 1, best_r = 128;
-  for (int r : {64, 128}) {
+  for (int r : {128}) {
     const int tl = 128 / r;  // waves of a workgroup that stream different tiles
     // at least one stage of tiles per wave per chunk, at most the CU count of workgroups
     const int64_t s_max = tiles / tl > 0 ? tiles / tl : 1;
@@ -140,8 +140,7 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   if (M > mla::kMaxRows || page_size % mla::kTile != 0 ||
       (int64_t)max_pages * page_size > 0x7FFFFFFFLL - 64)
     return MLA_ERR_UNSUPPORTED;
-  if (rows_per_group != 0 && rows_per_group != 64 && rows_per_group != 128)
-    return MLA_ERR_UNSUPPORTED;
+  if (rows_per_group != 0 && rows_per_group != 128) return MLA_ERR_UNSUPPORTED;
   int S = num_splits, r = rows_per_group;
   if (S == 0 || r == 0) {
     if (max_seq_len < 1) return MLA_ERR_INVALID_ARG;

@@ -74,7 +74,7 @@ mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t 
  * idle; the count has to follow the machine and the shape).  Chooses, from the compute-unit
  * count, the batch, the number of query rows (q_tokens * heads) and the longest context:
  *   *num_splits      S, the number of KV chunks per request (>= 1);
- *   *rows_per_group  query rows handled by one workgroup: 64 or 128.  Rows are the
+ *   *rows_per_group  query rows handled by one workgroup (128).  Rows are the
  *                    (query token, head) pairs of a request in [Sq, H] order; a request's
  *                    rows are covered by ceil(Sq*H / rows_per_group) workgroups per chunk,
  *                    which read the chunk's KV through the same L2;
@@ -113,7 +113,7 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
  * page_table[b] = {b}.
  *   max_seq_len   : host upper bound of the lengths, used only when num_splits == 0.
  *   num_splits    : S >= 1, or 0 to take the planner's choice for (B, Sq, H, max_seq_len).
- *   rows_per_group: 64 or 128, or 0 to take the planner's choice.
+ *   rows_per_group: 128, or 0 to take the planner's choice.
  *   partial_rows_capacity : entries the partial buffers hold (see mla_splitkv_plan).
  * Supported: 1 <= Sq, Sq*H <= 65536, page_size a positive multiple of 32, max_pages >= 1.
  * Errors: INVALID_ARG (NULL pointers with B > 0, negative sizes, scales not finite and > 0);

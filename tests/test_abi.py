@@ -72,7 +72,7 @@ def test_quantize_rejects_bad_arguments(lib):
 
 def _decode(lib, **kw):
     a = dict(q=FAKE, kv=FAKE, pt=FAKE, sl=FAKE, B=1, Sq=1, H=16, P=64, maxp=4, maxl=256,
-             qs=1.0, ks=1.0, sm=0.07, S=4, r=64, po=FAKE, pl=FAKE, cap=1 << 20)
+             qs=1.0, ks=1.0, sm=0.07, S=4, r=128, po=FAKE, pl=FAKE, cap=1 << 20)
     a.update(kw)
     return lib.mla_decode_splitkv(a["q"], a["kv"], a["pt"], a["sl"], a["B"], a["Sq"], a["H"],
                                   a["P"], a["maxp"], a["maxl"], a["qs"], a["ks"], a["sm"],
@@ -104,6 +104,7 @@ def test_decode_unsupported_shapes_and_workspace(lib):
     assert _decode(lib, Sq=2, H=40000) == UNSUPPORTED   # more than 65536 rows
     assert _decode(lib, r=48) == UNSUPPORTED
     assert _decode(lib, r=32) == UNSUPPORTED
+    assert _decode(lib, r=64) == UNSUPPORTED
     assert _decode(lib, S=70000) == UNSUPPORTED
     assert _decode(lib, cap=4 * 16 - 1) == WORKSPACE    # B*S*Sq*H = 64 entries needed
     assert _decode(lib, B=0, q=None, kv=None) == OK     # empty batch: nothing enqueued
@@ -138,7 +139,7 @@ def test_plan_rejects_bad_arguments(lib):
                                       (1, 1, 16, 256), (3, 2, 48, 5000)])
 def test_plan_fills_the_machine_and_is_consistent(lib, B, Sq, H, L):
     st, S, r, n = _plan(lib, B, Sq, H, L, 256)
-    assert st == OK and S >= 1 and r in (64, 128)
+    assert st == OK and S >= 1 and r == 128
     assert n == B * S * Sq * H
     G = -(-(Sq * H) // r)
     tiles = -(-L // 32)

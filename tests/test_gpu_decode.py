@@ -63,15 +63,15 @@ def _compare(dw, got_o, got_l, ref, heads=None):
 
 SMALL = [
     # name, B, H, Sq, lens, page_size, permuted, splits, rows_per_group
-    ("one_token", 1, 16, 1, [1], 0, False, 1, 64),
+    ("one_token", 1, 16, 1, [1], 0, False, 1, 128),
     ("ragged_tail", 2, 16, 1, [33, 95], 0, False, 2, 128),
-    ("several_tiles_h48", 1, 48, 1, [1000], 0, False, 3, 64),
-    ("causal_sq2", 2, 16, 2, [2, 70], 0, False, 1, 64),
-    ("causal_sq8_paged", 3, 32, 8, [8, 300, 129], 64, True, 4, 64),
+    ("several_tiles_h48", 1, 48, 1, [1000], 0, False, 3, 128),
+    ("causal_sq2", 2, 16, 2, [2, 70], 0, False, 1, 128),
+    ("causal_sq8_paged", 3, 32, 8, [8, 300, 129], 64, True, 4, 128),
     ("paged_p32", 4, 64, 1, [31, 64, 65, 2049], 32, True, 5, 128),
     ("rows_128", 1, 128, 1, [4500], 0, False, 8, 128),
-    ("h256_rows64", 2, 256, 1, [700, 1300], 64, True, 3, 64),
-    ("more_splits_than_tiles", 1, 16, 1, [100], 0, False, 16, 64),
+    ("h256_rows64", 2, 256, 1, [700, 1300], 64, True, 3, 128),
+    ("more_splits_than_tiles", 1, 16, 1, [100], 0, False, 16, 128),
 ]
 
 
@@ -90,7 +90,7 @@ def test_empty_request_and_short_context():
     w = Workload("edge", batch=3, heads=16, q_tokens=4, context=None, context_range=(1, 1),
                  page_size=64, permuted_pool=True, seed=5)
     dw = materialize(w, seq_lens=np.array([0, 2, 80], np.int32))
-    o, l, _ = _run(dw, 3, 64)
+    o, l, _ = _run(dw, 3, 128)
     assert np.all(o[0] == 0) and np.all(l[0] == -np.inf)       # nothing to attend to
     # L = 2 < Sq = 4: query tokens 0 and 1 see nothing, tokens 2 and 3 see 1 and 2 positions
     assert np.all(o[1][:2] == 0) and np.all(l[1][:2] == -np.inf)
@@ -113,7 +113,7 @@ def test_split_count_does_not_change_the_answer():
     dw = materialize(w)
     ref = _oracle(dw, [0])
     outs = []
-    for S, r in [(1, 64), (2, 128), (7, 64), (64, 128), (256, 64)]:
+    for S, r in [(1, 128), (2, 128), (7, 128), (64, 128), (256, 128)]:
         o, l, _ = _run(dw, S, r)
         _compare(dw, o, l, ref)
         outs.append(o)

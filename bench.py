@@ -2,22 +2,29 @@
 """Benchmark: FP8 MLA split-KV decode on one MI355X.
 
 One step = the whole hot path for one decode step of one MLA layer: saturating FP8
-quantisation of the step's Q, split-KV partial attention over the FP8 KV cache, and the
-log-sum-exp combine to bf16.  KV and Q are resident in HBM before timing starts.  The KV
-cache is held in several identical copies that the steps rotate through, so that no step
-finds its KV in the 256 MB Infinity Cache left behind by the previous one.
+quantisation of the step's Q (fp32 -> e4m3), split-KV partial attention over the FP8 KV
+cache, and the log-sum-exp combine to bf16.  Q (fp32) and the FP8 KV cache are resident in
+HBM before timing starts.  The KV cache is held in several identical copies that consecutive
+steps rotate through (at least 512 MiB in total), so that no step finds its KV in the
+256 MiB Infinity Cache left behind by the previous one.
+
+The timed steps are captured once in a HIP graph (torch.cuda.CUDAGraph) and replayed, so
+host launch overhead is not part of the measurement; the region is bracketed by a device
+synchronisation and HIP events on the launch stream.  The decode kernel's own duration for
+the roofline comes from a second graph that holds only decode launches, timed the same way.
 
 Prints one JSON line.  `value` is microseconds per decode step on the batch-1, 128K-context
 workload; the batch-16 workload is reported alongside.  `roofline` is for the decode kernel
-(HBM-bound at 1 query token per request): algorithmic bytes = KV bytes + Q bytes per launch,
-divided by the kernel's average duration from HIP events on its stream.
+(HBM-bound at one query token per request): algorithmic bytes = KV bytes + Q bytes per
+launch (576 B per cached token, 576 B per query row), divided by its average duration.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -25,6 +32,8 @@ import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "µs/decode step + achieved KV-read HBM GB/s (% of peak), 128K ctx batch 1/16"
 
 
 def _parse():
@@ -33,11 +42,15 @@ def _parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="b1_128k")
-    ap.add_argument("--also", default="b16_128k", help="second workload reported alongside ('' = none)")
+    ap.add_argument("--also", default="b16_128k",
+                    help="second workload reported alongside ('' = none)")
     ap.add_argument("--splits", type=int, default=0, help="0 = planner")
     ap.add_argument("--rows-per-group", type=int, default=0, help="0 = planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from Python instead of replaying graphs "
+                         "(what a profiler run needs to see individual launches clearly)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, --steps times (the "
                          "reference kernel that calibrates HBM byte counters), then exit")
@@ -57,7 +70,22 @@ def copy_probe(mib, steps):
     print(json.dumps({"copy_probe_bytes": n, "launches": steps}), flush=True)
 
 
-def run_workload(key, steps, warmup, splits, rows_per_group, min_bytes=512 << 20):
+def _time_graph(g, reps):
+    """Average milliseconds of one replay of g over reps replays (HIP events on the stream
+    the graph is launched on)."""
+    import torch
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_bytes=512 << 20):
     import torch
     import fp8_mla_split_amd as mla
     from fp8_mla_split_amd.workload import materialize
@@ -74,61 +102,83 @@ def run_workload(key, steps, warmup, splits, rows_per_group, min_bytes=512 << 20
     plan = mla.splitkv_plan(B, Sq, H, dw.max_seq_len)
     S = splits or plan.num_splits
     r = rows_per_group or plan.rows_per_group
-    po = torch.empty((B, S, Sq * H, 512), dtype=torch.float32, device="cuda")
+    po = torch.empty((B, S, Sq * H, 512), dtype=torch.float16, device="cuda")
     pl = torch.empty((B, S, Sq * H), dtype=torch.float32, device="cuda")
     out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Sq, H), dtype=torch.float32, device="cuda")
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def quantize():
         mla.quantize_fp8_sat(q32, dw.q_scale, out=q8)
-        if ev is not None:
-            ev[1].record()
+
+    def decode(i):
         mla.decode_splitkv(q8, pools[i % copies], dw.page_table, dw.seq_lens, dw.q_scale,
                            dw.kv_scale, w.softmax_scale, dw.max_seq_len, S, r, po, pl)
-        if ev is not None:
-            ev[2].record()
-        mla.splitkv_combine(po, pl, Sq, H, out=out, out_lse=lse)
-        if ev is not None:
-            ev[3].record()
+
+    def combine():
+        mla.splitkv_combine(po, pl, Sq, H, dw.kv_scale, out=out, out_lse=lse)
+
+    def step(i):
+        quantize()
+        decode(i)
+        combine()
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        step(i, evs[i])
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    q_us = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    dec_us = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    comb_us = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
-    step_us = np.array([e[0].elapsed_time(e[3]) for e in evs]) * 1e3
+
+    res = {"workload": w.name, "batch": B, "heads": H, "q_tokens": Sq,
+           "context": int(dw.max_seq_len), "kv_tokens": dw.kv_tokens, "num_splits": S,
+           "rows_per_group": r, "kv_copies": copies, "timing": "eager" if eager else "hip_graph"}
+    if eager:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            evs[i][0].record()
+            quantize()
+            evs[i][1].record()
+            decode(i)
+            evs[i][2].record()
+            combine()
+            evs[i][3].record()
+        t1.record()
+        torch.cuda.synchronize()
+        step_us = t0.elapsed_time(t1) * 1e3 / steps
+        q_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        dec_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+        comb_us = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
+    else:
+        stream = torch.cuda.Stream()
+        graphs = {}
+        for name, fn in (("step", step), ("quantize", lambda i: quantize()), ("decode", decode),
+                         ("combine", lambda i: combine())):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(steps):
+                    fn(i)
+            graphs[name] = g
+        for g in graphs.values():  # one untimed replay each
+            g.replay()
+        torch.cuda.synchronize()
+        step_us = _time_graph(graphs["step"], 3) * 1e3 / steps
+        q_us = _time_graph(graphs["quantize"], 3) * 1e3 / steps
+        dec_us = _time_graph(graphs["decode"], 3) * 1e3 / steps
+        comb_us = _time_graph(graphs["combine"], 3) * 1e3 / steps
+        del graphs
 
     q_bytes = B * Sq * H * 576
     algo = kv_bytes + q_bytes
     flops = 2.0 * B * Sq * H * dw.kv_tokens * (576 + 512)  # QK^T + PV, algorithmic
-    res = {
-        "workload": w.name, "batch": B, "heads": H, "q_tokens": Sq,
-        "context": int(dw.max_seq_len), "kv_tokens": dw.kv_tokens,
-        "num_splits": S, "rows_per_group": r, "kv_copies": copies,
-        "us_per_step": total_ms * 1e3 / steps,
-        "step_us_p10_p50_p90": [float(np.percentile(step_us, p)) for p in (10, 50, 90)],
-        "quantize_q_us": float(q_us.mean()), "decode_us": float(dec_us.mean()),
-        "combine_us": float(comb_us.mean()),
-        "decode_us_p50": float(np.median(dec_us)),
+    res.update({
+        "us_per_step": step_us,
+        "quantize_q_us": q_us, "decode_us": dec_us, "combine_us": comb_us,
         "kv_bytes": kv_bytes, "algo_bytes_decode": algo,
-        "decode_gbps": algo / (dec_us.mean() * 1e3),
-        "step_kv_gbps": kv_bytes / (total_ms * 1e6 / steps),
-        "decode_mfma_tflops_algorithmic": flops / (dec_us.mean() * 1e6),
-        "partial_bytes": B * S * Sq * H * 513 * 4,
-    }
+        "decode_gbps": algo / (dec_us * 1e3),
+        "step_kv_gbps": kv_bytes / (step_us * 1e3),
+        "decode_mfma_tflops_algorithmic": flops / (dec_us * 1e6),
+        "partial_bytes": B * S * Sq * H * (512 * 2 + 4),
+    })
     del pools, po, pl, dw
     torch.cuda.empty_cache()
     return res
@@ -136,10 +186,9 @@ def run_workload(key, steps, warmup, splits, rows_per_group, min_bytes=512 << 20
 
 def cpu_baseline(key, budget_s):
     """The oracle as it stands, one decode step at a time on the host cores, until about
-    budget_s seconds of work are done (the sample is a count of whole steps)."""
-    from oracle import attention_fp64, quantize_e4m3_sat
+    budget_s seconds of work are done (the sample is a count of whole steps of request 0)."""
+    from oracle import attention_fp64, per_tensor_scale, quantize_e4m3_sat
     from synthetic import WORKLOADS, kv_request_f32, page_layout, q_f32, seq_lens_for
-    from oracle import per_tensor_scale
 
     w = WORKLOADS[key]
     lens = seq_lens_for(w)
@@ -156,51 +205,73 @@ def cpu_baseline(key, budget_s):
         attention_fp64(q8, qs, pool, ks, table[:1], lens[:1], P, w.softmax_scale)
         n += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or n >= 50:
+        if el >= budget_s or n >= 200:
             break
     try:
         from threadpoolctl import threadpool_info
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info())
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    steps_per_request = w.batch  # the oracle handles requests one after another
-    us = el / n * 1e6 * steps_per_request
-    return {"value": us, "unit": "us/step", "cores": cores, "kind": "oracle",
+    us = el / n * 1e6 * w.batch  # the oracle handles requests one after another
+    return {"value": round(us, 1), "unit": "us/step", "cores": cores, "kind": "oracle",
             "sample": f"{n} full decode steps of request 0 of {w.name} (Q quantize + fp64 "
                       f"attention over all {int(lens[0])} positions and {w.heads} heads), "
                       f"{el:.1f} s of host time"}
+
+
+def decode_source_hash():
+    with open(os.path.join(ROOT, "fp8_mla_split_amd", "csrc", "decode.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per decode launch from the committed profiler counters, if they were taken
+    on the decode kernel as it is now (same source hash) and on this workload; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_kernel_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), flags=re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("decode_source_sha256_16") != decode_source_hash():
+        return None
+    return rec.get("bytes_per_launch", {}).get(workload)
 
 
 def main():
     a = _parse()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
-              f"(multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+              f"(how the path would shard over GPUs is described, not built)", file=sys.stderr)
         sys.exit(2)
+    if a.copy_probe_mib:
+        copy_probe(a.copy_probe_mib, a.steps)
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    if a.copy_probe_mib:
-        copy_probe(a.copy_probe_mib, a.steps)
-        return
+    sys.path.insert(0, ROOT)
     t_wall = time.time()
-    main_res = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group)
-    print(f"[bench] {a.workload}: {main_res['us_per_step']:.2f} us/step "
-          f"(decode {main_res['decode_us']:.2f} us, {main_res['decode_gbps']:.0f} GB/s)",
+    main_res = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager)
+    print(f"[bench] {a.workload}: {main_res['us_per_step']:.2f} us/step (decode "
+          f"{main_res['decode_us']:.2f} us, {main_res['decode_gbps']:.0f} GB/s; combine "
+          f"{main_res['combine_us']:.2f} us; Q quantize {main_res['quantize_q_us']:.2f} us)",
           file=sys.stderr, flush=True)
     also = None
     if a.also:
-        also = run_workload(a.also, max(20, a.steps // 4), max(5, a.warmup // 4), 0, 0)
-        print(f"[bench] {a.also}: {also['us_per_step']:.2f} us/step "
-              f"(decode {also['decode_us']:.2f} us, {also['decode_gbps']:.0f} GB/s)",
+        also = run_workload(a.also, max(20, a.steps // 4), max(5, a.warmup // 4), 0, 0, a.eager)
+        print(f"[bench] {a.also}: {also['us_per_step']:.2f} us/step (decode "
+              f"{also['decode_us']:.2f} us, {also['decode_gbps']:.0f} GB/s)",
               file=sys.stderr, flush=True)
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(a.workload, a.cpu_seconds)
     achieved = main_res["decode_gbps"]
+    traffic = measured_traffic(main_res["workload"])
     line = {
-        "metric": "µs/decode step + achieved KV-read HBM GB/s (% of peak), 128K ctx batch 1/16",
+        "metric": METRIC,
         "value": round(main_res["us_per_step"], 3),
         "unit": "us/step",
         "n_gpus": 1,
@@ -213,14 +284,15 @@ def main():
         "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
         "data": "synthetic (seeded N(0,1) Q/KV, per-tensor scales)",
         "config": {k: main_res[k] for k in ("workload", "batch", "heads", "q_tokens", "context",
-                                            "num_splits", "rows_per_group", "kv_copies")},
+                                            "num_splits", "rows_per_group", "kv_copies",
+                                            "timing")},
         "kv_read_gbps_step": round(main_res["step_kv_gbps"], 1),
         "kv_read_pct_of_peak_step": round(100 * main_res["step_kv_gbps"] / HBM_PEAK_GBPS, 2),
         "breakdown_us": {k: round(main_res[k], 3) for k in ("quantize_q_us", "decode_us",
                                                             "combine_us")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
+                     "traffic": traffic,
                      "kernel": "decode_kernel (mla_decode_splitkv)",
                      "algorithmic_bytes_per_launch": main_res["algo_bytes_decode"],
                      "mfma_tflops_algorithmic": round(main_res["decode_mfma_tflops_algorithmic"], 1),
@@ -229,8 +301,10 @@ def main():
         "also": None if also is None else {
             "workload": also["workload"], "us_per_step": round(also["us_per_step"], 3),
             "decode_us": round(also["decode_us"], 3),
+            "combine_us": round(also["combine_us"], 3),
             "decode_gbps": round(also["decode_gbps"], 1),
             "decode_frac_of_hbm_peak": round(also["decode_gbps"] / HBM_PEAK_GBPS, 4),
+            "step_kv_gbps": round(also["step_kv_gbps"], 1),
             "num_splits": also["num_splits"], "rows_per_group": also["rows_per_group"]},
         "detail": main_res,
         "wall_s": round(time.time() - t_wall, 1),

@@ -543,11 +543,11 @@ void decode_kernel(const DecodeParams p) {
     rs.mu = rs.m_true;
   }
 
-  // ---- normalise, write partial O and lse
+  // ---- normalise, write partial O (fp16, in units of kv_scale: |O| <= 448) and lse
   const float mu = rs.mu;
   const f32x2 lpair = row_pair(rs.l_run);
   const float Ls = lpair[0] + lpair[1];  // both halves of the row
-  const float f = (mu != -INFINITY && Ls > 0.f) ? p.kv_scale / Ls : 0.f;
+  const float f = (mu != -INFINITY && Ls > 0.f) ? 1.0f / Ls : 0.f;
   if (lane < 32 && row_ok)
     p.partial_lse[prow + R] = Ls > 0.f ? (mu + log2f(Ls) - kLog2PScale) * kLn2 : -INFINITY;
 
@@ -558,13 +558,14 @@ void decode_kernel(const DecodeParams p) {
   for (int r = 0; r < 16; ++r) fr[r] = __shfl(f, tok_of(gg, r));
 
   // register r of block d is row wrow0 + tok_of(gg, r), column 32 d + n
-  float* wout = p.partial_o + (prow + wrow0) * kDv + n;
+  _Float16* wout = (_Float16*)p.partial_o + (prow + wrow0) * kDv + n;
   if (wrow0 + 32 <= M) {
 #pragma unroll
     for (int d = 0; d < 16; ++d) {
       const f32x16 v = from_acc(o[d]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) wout[tok_of(gg, r) * kDv + 32 * d] = v[r] * fr[r];
+      for (int r = 0; r < 16; ++r)
+        wout[tok_of(gg, r) * kDv + 32 * d] = (_Float16)(v[r] * fr[r]);
     }
   } else {
 #pragma unroll
@@ -572,7 +573,8 @@ void decode_kernel(const DecodeParams p) {
       const f32x16 v = from_acc(o[d]);
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (wrow0 + tok_of(gg, r) < M) wout[tok_of(gg, r) * kDv + 32 * d] = v[r] * fr[r];
+        if (wrow0 + tok_of(gg, r) < M)
+          wout[tok_of(gg, r) * kDv + 32 * d] = (_Float16)(v[r] * fr[r]);
     }
   }
 }

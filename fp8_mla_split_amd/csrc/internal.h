@@ -16,7 +16,7 @@ struct DecodeParams {
   const uint8_t* kv;
   const int32_t* page_table;
   const int32_t* seq_lens;
-  float* partial_o;
+  uint16_t* partial_o;                // fp16 bits, in units of kv_scale
   float* partial_lse;
   int batch, q_tokens, heads, rows;   // rows = q_tokens * heads
   int page_size, max_pages, num_splits, groups;
@@ -26,7 +26,7 @@ struct DecodeParams {
 
 hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scale, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t s);
-hipError_t launch_combine(const float* po, const float* pl, int batch, int splits, int rows,
-                          uint16_t* out, float* out_lse, hipStream_t s);
+hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
+                          float v_scale, uint16_t* out, float* out_lse, hipStream_t s);
 
 }  // namespace mla

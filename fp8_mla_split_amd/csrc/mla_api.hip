@@ -29,52 +29,41 @@ bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Planner cost model.  Work is MFMA-bound per workgroup and HBM-bound overall; every split
-// adds one fp32 partial row per query row (written by the decode kernel, read back by the
-// combine), and every extra row group per split re-reads the split's KV from L2.  Estimates
-// are in nanoseconds on round numbers for an MI355X-class part (8 TB/s HBM, ~30 TB/s L2,
-// ~3.5 PFLOP/s of sustained FP8 MFMA); only their ratios matter.
-double plan_cost(int64_t B, int64_t M, int64_t L, int cu, int rows_per_group, int64_t S) {
-  const int64_t G = cdiv(M, rows_per_group);
+// Planner cost model, in microseconds, with rates measured on MI355X for the decode kernel
+// (one workgroup per CU; a 64-token step of 128 query rows takes ~2.8 us) plus the traffic
+// of the split partials (written by the decode kernel, read back by the combine).  Every
+// request is assumed to be max_seq_len long.
+constexpr double kStepUs = 2.8;             // one 64-token step of one workgroup
+constexpr double kWgOverheadUs = 3.0;       // staging before the first step, epilogue
+constexpr double kPartialBytesPerUs = 5e6;  // partial rows written + read back
+constexpr double kCombineUs = 3.0;          // the combine launch itself
+
+double plan_cost(int64_t B, int64_t M, int64_t L, int cu, int64_t S) {
+  const int64_t G = cdiv(M, 128);
   const int64_t tiles = cdiv(L, 32);
-  const int64_t per = cdiv(tiles, S);                       // tiles per chunk
-  const int64_t wgs = B * S * G;
-  const double waves = (double)cdiv(wgs, cu);               // workgroup rounds per CU
-  const double kv = (double)B * L * 576.0;
-  const double t_hbm = kv / 8.0e3;                          // bytes / (bytes per ns)
-  const double t_l2 = kv * (double)G / 30.0e3;
-  // per workgroup: per tiles of 32 tokens x rows_per_group rows, QK + hi/lo PV flops
-  const double wg_flops = (double)per * 32.0 * rows_per_group * 2.0 * (576.0 + 1024.0);
-  const double t_mfma = waves * wg_flops / (3.5e6 / cu);    // flops / (flops per ns per CU)
-  const double partial = (double)B * S * M * 513.0 * 4.0 * 2.0;  // write + read back
-  const double t_part = partial / 6.0e3;
-  double t = t_hbm;
-  if (t_l2 > t) t = t_l2;
-  if (t_mfma > t) t = t_mfma;
-  return t + t_part + 2000.0 * (S > 1);                     // + combine launch
+  const int64_t steps = cdiv(cdiv(tiles, S), 2);
+  const int64_t rounds = cdiv(B * S * G, cu);
+  const double t_dec = (double)rounds * (kWgOverheadUs + (double)steps * kStepUs);
+  const double t_part = (double)(B * S * M) * (1024.0 + 4.0) * 2.0 / kPartialBytesPerUs;
+  return t_dec + t_part + (S > 1 ? kCombineUs : 0.0);
 }
 
 mla_status plan(int batch, int q_tokens, int heads, int max_seq_len, int cu, int* splits,
                 int* rows_per_group) {
   const int64_t M = (int64_t)q_tokens * heads;
   const int64_t tiles = cdiv(max_seq_len, 32);
+  const int64_t s_max = tiles / 2 > 0 ? tiles / 2 : 1;  // at least one full step per chunk
   double best = -1.0;
-  int best_s = 1, best_r = 128;
-  for (int r : {128}) {
-    const int tl = 128 / r;  // waves of a workgroup that stream different tiles
-    // at least one stage of tiles per wave per chunk, at most the CU count of workgroups
-    const int64_t s_max = tiles / tl > 0 ? tiles / tl : 1;
-    for (int64_t S = 1; S <= s_max && S <= 4096; S = S < 8 ? S + 1 : S + S / 8) {
-      const double c = plan_cost(batch, M, max_seq_len, cu, r, S);
-      if (best < 0.0 || c < best) {
-        best = c;
-        best_s = (int)S;
-        best_r = r;
-      }
+  int best_s = 1;
+  for (int64_t S = 1; S <= s_max && S <= 4096; ++S) {
+    const double c = plan_cost(batch, M, max_seq_len, cu, S);
+    if (best < 0.0 || c < best) {
+      best = c;
+      best_s = (int)S;
     }
   }
   *splits = best_s;
-  *rows_per_group = best_r;
+  *rows_per_group = 128;
   return MLA_OK;
 }
 
@@ -124,7 +113,7 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                               const int32_t* page_table_dev, const int32_t* seq_lens_dev,
                               int batch, int q_tokens, int heads, int page_size, int max_pages,
                               int max_seq_len, float q_scale, float kv_scale, float softmax_scale,
-                              int num_splits, int rows_per_group, float* partial_o_dev,
+                              int num_splits, int rows_per_group, uint16_t* partial_o_dev,
                               float* partial_lse_dev, int64_t partial_rows_capacity,
                               void* stream) {
   if (batch < 0 || q_tokens < 1 || heads < 1 || page_size < 1 || max_pages < 1 ||
@@ -178,17 +167,18 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status mla_splitkv_combine(const float* partial_o_dev, const float* partial_lse_dev,
-                               int batch, int num_splits, int q_tokens, int heads,
+mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* partial_lse_dev,
+                               int batch, int num_splits, int q_tokens, int heads, float v_scale,
                                uint16_t* out_bf16_dev, float* out_lse_dev, void* stream) {
   if (batch < 0 || num_splits < 1 || q_tokens < 1 || heads < 1) return MLA_ERR_INVALID_ARG;
+  if (!good_scale(v_scale)) return MLA_ERR_INVALID_ARG;
   if (batch == 0) return MLA_OK;
   if (!partial_o_dev || !partial_lse_dev || !out_bf16_dev) return MLA_ERR_INVALID_ARG;
   const int64_t M = (int64_t)q_tokens * heads;
   if (M > mla::kMaxRows || num_splits > mla::kMaxSplitsCombine) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)batch * M * 2 > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
   const hipError_t e = mla::launch_combine(partial_o_dev, partial_lse_dev, batch, num_splits,
-                                           (int)M, out_bf16_dev, out_lse_dev,
+                                           (int)M, v_scale, out_bf16_dev, out_lse_dev,
                                            (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -32,7 +32,7 @@ _lib.mla_decode_splitkv.restype = _i32
 _lib.mla_decode_splitkv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _f32, _f32, _f32, _i32, _i32, _vp, _vp, _i64, _vp]
 _lib.mla_splitkv_combine.restype = _i32
-_lib.mla_splitkv_combine.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+_lib.mla_splitkv_combine.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]
 
 D_KV, D_V = 576, 512
 
@@ -102,8 +102,8 @@ def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.T
     """Split-KV partial attention.  Returns ``(partial_o, partial_lse, num_splits)``.
 
     q8 [B, Sq, H, 576] uint8; kv_pool8 [pages, page_size, 576] uint8; page_table
-    [B, max_pages] int32; seq_lens [B] int32.  partial_o [B, S, Sq*H, 512] fp32 and
-    partial_lse [B, S, Sq*H] fp32 are allocated when not given.
+    [B, max_pages] int32; seq_lens [B] int32.  partial_o [B, S, Sq*H, 512] fp16 (in units of
+    kv_scale) and partial_lse [B, S, Sq*H] fp32 are allocated when not given.
     """
     _dev_tensor(q8, torch.uint8, "q8")
     _dev_tensor(kv_pool8, torch.uint8, "kv_pool8")
@@ -119,11 +119,11 @@ def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.T
         rows_per_group = rows_per_group or plan.rows_per_group
     rows = Sq * H
     if partial_o is None:
-        partial_o = torch.empty((B, num_splits, rows, D_V), dtype=torch.float32,
+        partial_o = torch.empty((B, num_splits, rows, D_V), dtype=torch.float16,
                                 device=q8.device)
     if partial_lse is None:
         partial_lse = torch.empty((B, num_splits, rows), dtype=torch.float32, device=q8.device)
-    _dev_tensor(partial_o, torch.float32, "partial_o")
+    _dev_tensor(partial_o, torch.float16, "partial_o")
     _dev_tensor(partial_lse, torch.float32, "partial_lse")
     cap = min(partial_o.numel() // D_V, partial_lse.numel())
     _check(_lib.mla_decode_splitkv(
@@ -135,10 +135,11 @@ def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.T
 
 
 def splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens: int,
-                    heads: int, out: Optional[torch.Tensor] = None,
+                    heads: int, v_scale: float, out: Optional[torch.Tensor] = None,
                     out_lse: Optional[torch.Tensor] = None, want_lse: bool = True):
-    """LSE merge -> (out [B, Sq, H, 512] bf16, lse [B, Sq, H] fp32 or None)."""
-    _dev_tensor(partial_o, torch.float32, "partial_o")
+    """LSE merge -> (out [B, Sq, H, 512] bf16, lse [B, Sq, H] fp32 or None).  partial_o is
+    fp16 in units of v_scale (the KV scale), as decode_splitkv writes it."""
+    _dev_tensor(partial_o, torch.float16, "partial_o")
     _dev_tensor(partial_lse, torch.float32, "partial_lse")
     B, S = partial_lse.shape[0], partial_lse.shape[1]
     if partial_lse.shape[2] != q_tokens * heads or partial_o.shape[:3] != partial_lse.shape:
@@ -152,7 +153,7 @@ def splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens
     if out_lse is not None:
         _dev_tensor(out_lse, torch.float32, "out_lse")
     _check(_lib.mla_splitkv_combine(_ptr(partial_o), _ptr(partial_lse), B, S, q_tokens, heads,
-                                    _ptr(out), _ptr(out_lse), _stream(dev)),
+                                    float(v_scale), _ptr(out), _ptr(out_lse), _stream(dev)),
            "mla_splitkv_combine")
     return out, out_lse
 
@@ -162,4 +163,4 @@ def decode(q8, kv_pool8, page_table, seq_lens, q_scale, kv_scale, softmax_scale,
     """Partial attention followed by the combine: (out bf16, lse fp32)."""
     po, pl, _ = decode_splitkv(q8, kv_pool8, page_table, seq_lens, q_scale, kv_scale,
                                softmax_scale, max_seq_len, num_splits, rows_per_group)
-    return splitkv_combine(po, pl, q8.shape[1], q8.shape[2])
+    return splitkv_combine(po, pl, q8.shape[1], q8.shape[2], kv_scale)

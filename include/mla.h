@@ -79,7 +79,7 @@ mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t 
  *                    rows are covered by ceil(Sq*H / rows_per_group) workgroups per chunk,
  *                    which read the chunk's KV through the same L2;
  *   *partial_rows    B * S * Sq * H: the entries mla_decode_splitkv writes, i.e. the sizes
- *                    of partial_o (x 512 floats) and partial_lse (x 1 float).
+ *                    of partial_o (x 512 fp16 values) and partial_lse (x 1 float).
  *   cu_count : compute units to plan for; 0 queries the current device (a HIP call).
  * Any output pointer may be NULL.  Errors: INVALID_ARG for batch, q_tokens, heads or
  * max_seq_len < 1 or cu_count < 0; UNSUPPORTED when q_tokens * heads > 65536.
@@ -96,10 +96,12 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
  * tokens):
  *   z_n  = softmax_scale * q_scale * kv_scale * (dec(Q8[b,t,h,:]) . dec(KV8[n,:]))
  *   partial_lse[b,s,r]    = log(sum_n exp(z_n))          (natural log; -inf if no position)
- *   partial_o[b,s,r,0:512] = sum_n softmax(z)_n * kv_scale * dec(KV8[n,0:512])
- * Chunk s holds tiles [s*c, (s+1)*c) of 32 tokens, c = ceil(ceil(L_b/32) / S).  Partial
- * outputs are fp32; where the lse is -inf (empty chunk, or no visible position) the
- * partial_o entry is unspecified.
+ *   partial_o[b,s,r,0:512] = sum_n softmax(z)_n * dec(KV8[n,0:512])
+ * i.e. the chunk's attention output in units of kv_scale, so every value lies in [-448, 448]
+ * and is stored as IEEE fp16 (round to nearest even); mla_splitkv_combine multiplies by
+ * kv_scale again.  Chunk s holds tiles [s*c, (s+1)*c) of 32 tokens,
+ * c = ceil(ceil(L_b/32) / S).  Where the lse is -inf (empty chunk, or no visible position)
+ * the partial_o entry is unspecified.
  *
  * Layouts (all contiguous, row-major):
  *   q8_dev          uint8 [B, Sq, H, 576]          e4m3 codes of Q
@@ -108,7 +110,7 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
  *                                          of page page_table[b, n / page_size]
  *   seq_lens_dev    int32 [B]              context length per request (device values are
  *                                          clamped to [0, max_pages * page_size])
- *   partial_o_dev   fp32 [B, S, Sq*H, 512];  partial_lse_dev fp32 [B, S, Sq*H]
+ *   partial_o_dev   fp16 bits [B, S, Sq*H, 512];  partial_lse_dev fp32 [B, S, Sq*H]
  * A contiguous per-request cache is the same call with page_size = the padded length and
  * page_table[b] = {b}.
  *   max_seq_len   : host upper bound of the lengths, used only when num_splits == 0.
@@ -125,24 +127,26 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                               int batch, int q_tokens, int heads, int page_size, int max_pages,
                               int max_seq_len, float q_scale, float kv_scale, float softmax_scale,
                               int num_splits, int rows_per_group,
-                              float* partial_o_dev, float* partial_lse_dev,
+                              uint16_t* partial_o_dev, float* partial_lse_dev,
                               int64_t partial_rows_capacity, void* stream);
 
 /*
  * Log-sum-exp merge of the split partials ([A/MLA] item (2)).  For each (b, r):
- *   M = max_s lse_s;  w_s = exp(lse_s - M);  O = sum_s w_s O_s / sum_s w_s;
+ *   M = max_s lse_s;  w_s = exp(lse_s - M);  O = v_scale * sum_s w_s O_s / sum_s w_s;
  *   lse = M + log(sum_s w_s)
  * Splits with lse_s = -inf are skipped (their partial_o is never read as a weight);
  * a row whose splits are all empty gives O = 0 and lse = -inf.  Each workgroup issues all
  * of a row's partial loads before it accumulates them in registers.
- *   partial_o_dev fp32 [B, S, R, 512], partial_lse_dev fp32 [B, S, R] with R = Sq * H;
+ *   partial_o_dev fp16 bits [B, S, R, 512] (as mla_decode_splitkv writes them, in units of
+ *                 v_scale), partial_lse_dev fp32 [B, S, R] with R = Sq * H;
+ *   v_scale       the KV dequantisation scale the partials were computed with (finite, > 0);
  *   out_bf16_dev  uint16 [B, Sq, H, 512]: bf16 bit patterns, round-to-nearest-even;
  *   out_lse_dev   fp32 [B, Sq, H] or NULL.
- * Errors: INVALID_ARG (NULL inputs/outputs with B > 0, sizes < 1); UNSUPPORTED (S > 4096 or
- * Sq*H > 65536); HIP.  B == 0 enqueues nothing.
+ * Errors: INVALID_ARG (NULL inputs/outputs with B > 0, sizes < 1, bad v_scale); UNSUPPORTED
+ * (S > 4096 or Sq*H > 65536); HIP.  B == 0 enqueues nothing.
  */
-mla_status mla_splitkv_combine(const float* partial_o_dev, const float* partial_lse_dev,
-                               int batch, int num_splits, int q_tokens, int heads,
+mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* partial_lse_dev,
+                               int batch, int num_splits, int q_tokens, int heads, float v_scale,
                                uint16_t* out_bf16_dev, float* out_lse_dev, void* stream);
 
 #ifdef __cplusplus

@@ -28,7 +28,7 @@ def lib():
                                        ctypes.c_float, ctypes.c_void_p]
     i, f, v, i64 = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64
     L.mla_decode_splitkv.argtypes = [v, v, v, v, i, i, i, i, i, i, f, f, f, i, i, v, v, i64, v]
-    L.mla_splitkv_combine.argtypes = [v, v, i, i, i, i, v, v, v]
+    L.mla_splitkv_combine.argtypes = [v, v, i, i, i, i, f, v, v, v]
     L.mla_splitkv_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
                                    ctypes.POINTER(i64)]
     return L
@@ -112,13 +112,15 @@ def test_decode_unsupported_shapes_and_workspace(lib):
 
 def test_combine_rejects_bad_arguments(lib):
     c = lib.mla_splitkv_combine
-    assert c(None, FAKE, 1, 4, 1, 16, FAKE, None, None) == INVALID
-    assert c(FAKE, None, 1, 4, 1, 16, FAKE, None, None) == INVALID
-    assert c(FAKE, FAKE, 1, 4, 1, 16, None, None, None) == INVALID
-    assert c(FAKE, FAKE, 1, 0, 1, 16, FAKE, None, None) == INVALID
-    assert c(FAKE, FAKE, -1, 4, 1, 16, FAKE, None, None) == INVALID
-    assert c(FAKE, FAKE, 1, 5000, 1, 16, FAKE, None, None) == UNSUPPORTED
-    assert c(None, None, 0, 4, 1, 16, None, None, None) == OK
+    assert c(None, FAKE, 1, 4, 1, 16, 1.0, FAKE, None, None) == INVALID
+    assert c(FAKE, None, 1, 4, 1, 16, 1.0, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, 1.0, None, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 0, 1, 16, 1.0, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, -1, 4, 1, 16, 1.0, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, 0.0, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, float("nan"), FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 5000, 1, 16, 1.0, FAKE, None, None) == UNSUPPORTED
+    assert c(None, None, 0, 4, 1, 16, 1.0, None, None, None) == OK
 
 
 def _plan(lib, B, Sq, H, L, cu):

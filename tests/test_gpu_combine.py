@@ -1,4 +1,10 @@
-"""GPU LSE combine in isolation on oracle-made partials (runs on an MI355X)."""
+"""GPU LSE combine in isolation on oracle-made partials (runs on an MI355X).
+
+The combine's inputs are fp16 partial rows in units of the KV scale (what the decode kernel
+writes), so the partials are rounded to fp16 here first and the oracle merges exactly those
+values; the GPU result may differ from it only by fp32 accumulation and the bf16 rounding of
+the output.
+"""
 import numpy as np
 import pytest
 import torch
@@ -11,20 +17,21 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("B,S,Sq,H", [(1, 1, 1, 16), (2, 3, 2, 16), (1, 64, 1, 128),
-                                      (3, 100, 1, 32), (1, 17, 8, 16)])
+                                      (3, 100, 1, 32), (1, 17, 8, 16), (1, 256, 1, 128)])
 def test_combine_matches_oracle(B, S, Sq, H):
     rng = np.random.default_rng(S * 7 + H)
     R = Sq * H
-    po = rng.standard_normal((B, S, R, 512)).astype(np.float32)
+    v_scale = np.float32(0.0123)
+    po = (rng.standard_normal((B, S, R, 512)) * 60).astype(np.float16)   # |x| well inside 448
     pl = (rng.standard_normal((B, S, R)) * 4).astype(np.float32)
     if S > 1:
         pl[:, ::3, :] = -np.inf                      # empty splits ...
         po[:, ::3, :, :] = np.nan                    # ... whose partial values are garbage
     pl[0, :, 0] = -np.inf                            # a row with nothing visible
-    o_ref, l_ref = combine_fp64(np.where(np.isnan(po), 0, po).astype(np.float64),
-                                pl.astype(np.float64))
+    po64 = np.where(np.isnan(po), 0, po).astype(np.float64) * float(v_scale)
+    o_ref, l_ref = combine_fp64(po64, pl.astype(np.float64))
     out, lse = mla.splitkv_combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
-                                   Sq, H)
+                                   Sq, H, float(v_scale))
     o = bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)).reshape(B, R, 512)
     o_ref = o_ref.reshape(B, R, 512)
     # bf16 rounding of the exact merge plus fp32 accumulation

@@ -32,7 +32,7 @@ def _run(dw, num_splits=0, rows_per_group=0):
     po, pl, S = mla.decode_splitkv(dw.q8, dw.kv_pool8, dw.page_table, dw.seq_lens, dw.q_scale,
                                    dw.kv_scale, dw.w.softmax_scale, dw.max_seq_len,
                                    num_splits, rows_per_group)
-    out, lse = mla.splitkv_combine(po, pl, dw.w.q_tokens, dw.w.heads)
+    out, lse = mla.splitkv_combine(po, pl, dw.w.q_tokens, dw.w.heads, dw.kv_scale)
     torch.cuda.synchronize()
     return _bf16(out), lse.cpu().numpy(), S
 

@@ -32,9 +32,9 @@
 // Math per step (per wave, 32 rows x 64 tokens), all on FP8 MFMA v_mfma_scale_f32_32x32x64:
 //  * S^T = K . Q^T per tile: tokens along M, rows along N, 576 = 9 x 64 channels along K;
 //    the two tiles' chains are interleaved.  Computing the transpose puts each lane's 16
-//    scores for one row exactly where the P.V step needs them as its A operand.  MFMA
-//    token m reads LDS row perm_row(m), so register r of lane half gg holds tile token
-//    2r + gg; the permutation makes the transposed V reads below conflict-free.
+//    scores for one row exactly where the P.V step needs them as an operand.  MFMA token m
+//    reads LDS row perm_row(m), so register r of lane half gg holds tile token 2r + gg; the
+//    permutation makes the transposed V reads below conflict-free.
 //  * Online softmax in base 2 against a fixed reference max mu per row (the max of the row's
 //    first step with a visible position), so the 256-register O is never rescaled.  Each
 //    step's probabilities are normalised per row by 2^-e (e = floor of the row's step max
@@ -43,14 +43,21 @@
 //    up more than kHeadroom above mu (fp32 range at risk), the workgroup recomputes its
 //    chunk once with mu = the true max.
 //  * P is encoded as hi = e4m3(p) and lo = e4m3(p - hi), both in the same units, and
-//    O += hi . V + lo . V as two MFMAs over the step's 64 tokens that share one V operand
-//    (P.V with about 7 bits of P mantissa; a single e4m3 P costs several times the 2e-3
-//    normalised-L1 budget against the fp64 oracle).
+//    O^T += V^T . hi^T + V^T . lo^T as two MFMAs over the step's 64 tokens that share one V
+//    operand (P.V with about 7 bits of P mantissa; a single e4m3 P costs several times the
+//    2e-3 normalised-L1 budget against the fp64 oracle).  With V as the first operand the
+//    accumulator holds O transposed: lane n owns row n, and each register four consecutive
+//    value columns, so the epilogue stores 8 bytes per lane and instruction.
 //  * V (the first 512 columns of the same tiles) is read transposed with ds_read_b64_tr_b8.
-//  * Software pipeline: the 18 QK MFMAs of step i+1 are issued before the 32 PV MFMAs of
-//    step i, the softmax of step i+1 is issued in the gaps between those PV MFMAs, the DMA
-//    of step i+3 between the QK MFMAs, and the per-step barrier right after the last PV
-//    MFMA, so the matrix pipe keeps working through it.
+//
+// Schedule.  One wave issues at most one instruction every ~4 clocks and an MFMA runs 64
+// clocks, so about a dozen other instructions fit behind each MFMA.  A step's 50 MFMAs are
+// therefore interleaved with all of the step's other work in near-equal shares: the 18 QK
+// MFMAs of step i+1 carry the K fragment reads, the hi/lo encoding of step i's
+// probabilities and the DMA of step i+3; the 32 PV MFMAs of step i carry the V fragment
+// reads and the max / exp2 / sum of step i+1's scores.  The per-step barrier follows the
+// last PV MFMA, so the matrix pipe keeps working through it.  Masking (sequence tail,
+// causal positions, tiles past the chunk) is a uniform branch taken only in the last steps.
 #include <type_traits>
 
 #include "internal.h"
@@ -84,7 +91,7 @@ constexpr int kVAhead = 2;                  // PV blocks whose V fragments are i
 __device__ __forceinline__ int perm_row(int m) {
   return (m & 0x18) | ((m & 3) << 1) | ((m >> 2) & 1);
 }
-// Token index held in register r of a 32x32 MFMA result by lanes of half gg.
+// Index along M held in register r of a 32x32 MFMA result by lanes of half gg.
 __device__ __forceinline__ int tok_of(int gg, int r) { return 8 * (r >> 2) + 4 * gg + (r & 3); }
 
 // 16 bytes per lane, global -> LDS at M0 + 16 * lane, with M0 = lds_addr + IMM (the
@@ -107,32 +114,35 @@ __device__ __forceinline__ void dma16_s(uint32_t lds_addr, uint32_t voff,
                : "memory", "m0", "scc");
 }
 
-// FP8 x FP8 32x32x64 MFMA with explicit register classes: the scores live in VGPRs and O in
+// FP8 x FP8 32x32x64 MFMAs with explicit register classes: the scores live in VGPRs and O in
 // AGPRs (left to itself the compiler puts every accumulator in AGPRs, which then do not
 // hold O).  The "memory" clobber keeps the LDS fragment reads where the source places them.
-// Hazards the compiler cannot see through the asm are covered explicitly: s_nop 1 before
-// each MFMA covers a VALU write of an operand just before it, and at least 24 wait states
-// separate the last MFMA of a chain from any non-MFMA reader of its result (mfma_drain2,
-// which takes the accumulators as operands: the compiler treats an asm output as ready at
+// Hazards the compiler cannot see through the asm are handled here: the QK operands come
+// straight from LDS reads (ordered by s_waitcnt, no VALU producer), the PV MFMAs take a
+// VALU-written scale and P bytes and wait two states first; a non-MFMA reader of an MFMA
+// result is placed at least two MFMAs (128 clocks) after it or behind an explicit drain
+// that takes the accumulators as operands (the compiler treats an asm output as ready at
 // once and would otherwise copy it straight after the MFMA).
 __device__ __forceinline__ f32x16 mfma_qk_first(const i32x8& a, const i32x8& b) {
   f32x16 d;
-  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
                : "=&v"(d)
                : "v"(a), "v"(b), "v"(127)
                : "memory");
   return d;
 }
 __device__ __forceinline__ void mfma_qk(f32x16& d, const i32x8& a, const i32x8& b) {
-  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
                : "+v"(d)
                : "v"(a), "v"(b), "v"(127)
                : "memory");
 }
-__device__ __forceinline__ void mfma_pv(f32x16& acc, const i32x8& a, const i32x8& b, int scale_a) {
+// acc (O^T block) += V^T . P^T: A = V fragment (scale 2^0), B = P bytes (scale 2^(sb-127)).
+__device__ __forceinline__ void mfma_pv(f32x16& acc, const i32x8& v, const i32x8& pbytes,
+                                        int scale_b) {
   asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
                : "+a"(acc)
-               : "v"(a), "v"(b), "v"(scale_a), "v"(127)
+               : "v"(v), "v"(pbytes), "v"(127), "v"(scale_b)
                : "memory");
 }
 __device__ __forceinline__ void mfma_drain2(f32x16& a, f32x16& b) {
@@ -160,8 +170,8 @@ __device__ __forceinline__ f32x16 from_acc(const f32x16& a) {
   asm volatile("" : "=v"(v) : "0"(a));
   return v;
 }
-// Keeps the compiler from moving instructions across this point (used to interleave the
-// softmax VALU work with the PV MFMAs in source order).
+// Keeps the compiler from moving instructions across this point (used to interleave VALU
+// and LDS work with the MFMAs in source order).
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int N>
@@ -183,19 +193,37 @@ __device__ __forceinline__ i32x8 cat8(const i32x4& a, const i32x4& b) {
   return (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// The four transposed 8-byte reads of a V fragment as one operand (built through a union:
+// an element-wise build makes the compiler shuffle bytes).
+union VFrag {
+  i32x2 h[4];
+  i32x8 v;
+};
+
 // Softmax state of one lane: its row's reference max, the running true max and its share of
 // the row's sum of 2^(x - mu) * 224.
 struct RowState {
   float mu, m_true, l_run;
 };
 
-// One step's scores and probabilities (tile a in sa, tile b in sb).
-struct StepTile {
-  f32x16 sa, sb;  // raw scores, then probabilities in place
-  float off;      // exp2 argument offset
-  float psum;
+// One step's scores (tile a, tile b), turned into probabilities in place.
+struct Probs {
+  f32x16 a, b;
+  float off;   // exp2 argument offset
+  float mpart; // running max over the scores (first max piece)
+  float psum;  // running sum of the probabilities
+  int ef;      // step exponent: P bytes are in units of 2^ef
+};
+
+// P bytes of a step: [tile a | tile b], hi and lo e4m3 terms.
+struct PBytes {
+  i32x8 hi, lo;
+};
+
+// What the P.V of a step needs: its P bytes and exponent.
+struct StepP {
+  PBytes pb;
   int ef;
-  i32x8 hi, lo;   // P bytes: [tile a | tile b]
 };
 
 // K fragments of one QK MFMA pair (tile a, tile b).
@@ -245,13 +273,23 @@ void decode_kernel(const DecodeParams p) {
   }
 
   const int wrow0 = row0 + wave * 32;
-  const int R = wrow0 + n;  // this lane's query row (score and P layout)
+  const int R = wrow0 + n;  // this lane's query row (score, P and O layout)
   const bool row_ok = R < M;
   // last visible position of the row (bottom-right causal); rows past M are never stored
   const int lim = row_ok ? L - p.q_tokens + R / p.heads : 0x7FFFFFFF;
   const int lim_min = L - p.q_tokens + wrow0 / p.heads;
   const int nsteps = (ntiles + 1) / 2;
+  // Steps 0 .. nplain-1 need no masking: both tiles in the chunk and every position visible
+  // to every row of this wave (tile 2j + 1 ends at (t_begin + 2j + 2) * 32 - 1 <= lim_min).
+  int nplain;
+  {
+    const int jv = ((lim_min + 1) >> 5) - t_begin - 2;  // 2j <= jv
+    nplain = min(jv < 0 ? 0 : jv / 2 + 1, ntiles / 2);
+  }
   const int P = p.page_size;
+  const int tpp = P / kTile;  // tiles per page
+  const int64_t pt_row = (int64_t)b * p.max_pages;
+  const int pe_last = (t_begin + ntiles - 1) / tpp;  // page-table entry of the chunk's last tile
 
   // ---- DMA lane offsets.  Of a tile's 19 DMA instructions, wave w issues k = w + 4 i
   // (i < 4, and i = 4 for waves 0..2): LDS bytes 1024 w + 4096 i of the slot.  Chunk
@@ -266,37 +304,64 @@ void decode_kernel(const DecodeParams p) {
   }
   const uint32_t wave_lds = lds_base + (uint32_t)wave * 1024u;
 
-  // Page of tile ti of the chunk (scalar load); tiles past the chunk map to a valid entry
-  // and load nothing.
-  auto page_of = [&](int ti) __attribute__((always_inline)) -> int {
-    const int t = min(ti, ntiles - 1);
-    return page_table[(int64_t)b * p.max_pages + ((t_begin + t) * kTile) / P];
+  // ---- page cursor: page-table entry and tile-within-page of tile 2j of the next step j
+  // to prepare, advanced two tiles per step without divisions.
+  int cur_pe = t_begin / tpp;
+  int cur_po = t_begin - cur_pe * tpp;
+  struct StepPages {
+    int page_a, po_a, page_b, po_b;
   };
-  auto issue_tile = [&](int ti, int page, uint32_t slot_lds, auto jc)
+  auto next_pages = [&]() __attribute__((always_inline)) -> StepPages {
+    StepPages sp;
+    int pe_b = cur_pe, po_b = cur_po + 1;
+    if (po_b >= tpp) { po_b = 0; ++pe_b; }
+    sp.po_a = cur_po;
+    sp.po_b = po_b;
+    sp.page_a = page_table[pt_row + min(cur_pe, pe_last)];
+    sp.page_b = page_table[pt_row + min(pe_b, pe_last)];
+    cur_po += 2;
+    if (cur_po >= tpp) { cur_po -= tpp; ++cur_pe; }
+    if (cur_po >= tpp) { cur_po -= tpp; ++cur_pe; }
+    return sp;
+  };
+  // rows of the chunk's tiles that lie before the chunk's end (and the sequence's) are loaded;
+  // the rest of a slot, and every tile past the chunk, reads as zeros
+  const int chunk_end = min(L, (t_begin + ntiles) * kTile);
+  auto tile_rsrc = [&](int ti, int page, int po) __attribute__((always_inline))
+      -> __amdgpu_buffer_rsrc_t {
+    const int T0 = (t_begin + ti) * kTile;
+    int rows = chunk_end - T0;
+    rows = rows < 0 ? 0 : rows;
+    rows = rows > kTile ? kTile : rows;
+    const int nrec = __builtin_amdgcn_readfirstlane(rows * kD);  // scalar, for the resource
+    const uint8_t* base = p.kv + (uint64_t)(uint32_t)page * (uint64_t)p.page_bytes +
+                          (uint32_t)po * (uint32_t)(kTile * kD);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, 0x00020000);
+  };
+  // DMA instructions i of tile slot j of a step slot (i = 4 only on waves 0..2)
+  auto tile_dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t slot_lds, auto jc, auto ic)
       __attribute__((always_inline)) {
-    constexpr int j = decltype(jc)::value;
-    const uint8_t* base = p.kv;
-    int nrec = 0;
-    if (ti < ntiles) {
-      const int T0 = (t_begin + ti) * kTile;
-      base = p.kv + ((int64_t)page * P + (T0 % P)) * kD;
-      nrec = min(kTile, L - T0) * kD;
-    }
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, 0x00020000);
-    dma16<j * kSlot + 0 * 4096>(slot_lds, voff[0], rsrc);
-    dma16<j * kSlot + 1 * 4096>(slot_lds, voff[1], rsrc);
-    dma16<j * kSlot + 2 * 4096>(slot_lds, voff[2], rsrc);
-    dma16<j * kSlot + 3 * 4096>(slot_lds, voff[3], rsrc);
-    if (wave < 3) dma16<j * kSlot + 4 * 4096>(slot_lds, voff[4], rsrc);
+    constexpr int j = decltype(jc)::value, i = decltype(ic)::value;
+    if (i < 4 || wave < 3) dma16<j * kSlot + i * 4096>(slot_lds, voff[i], rsrc);
   };
-  // Both tiles of step st into its step slot.  Every step is issued, also past the end of
-  // the chunk (those load nothing and write zeros into a free slot), so the number of DMA
-  // instructions in flight behind any step is fixed and every wait below is a constant.
-  auto issue_step = [&](int st, int pg0, int pg1) __attribute__((always_inline)) {
-    const uint32_t slot_lds = wave_lds + (uint32_t)((st % kStepSlots) * 2 * kSlot);
-    issue_tile(2 * st, pg0, slot_lds, std::integral_constant<int, 0>{});
-    issue_tile(2 * st + 1, pg1, slot_lds, std::integral_constant<int, 1>{});
+  auto issue_tile = [&](int ti, int page, int po, uint32_t slot_lds, auto jc)
+      __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(ti, page, po);
+    tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 0>{});
+    tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 1>{});
+    tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 2>{});
+    tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 3>{});
+    tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 4>{});
+  };
+  // Every step is issued, also past the end of the chunk (those load nothing and write zeros
+  // into a free slot), so the number of DMA instructions in flight behind any step is fixed
+  // and every wait below is a constant.
+  auto slot_of = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    return wave_lds + (uint32_t)((st % kStepSlots) * 2 * kSlot);
+  };
+  auto issue_step = [&](int st, const StepPages& sp) __attribute__((always_inline)) {
+    issue_tile(2 * st, sp.page_a, sp.po_a, slot_of(st), std::integral_constant<int, 0>{});
+    issue_tile(2 * st + 1, sp.page_b, sp.po_b, slot_of(st), std::integral_constant<int, 1>{});
   };
 
   const int G16 = lane >> 4, i16 = lane & 15;
@@ -323,83 +388,101 @@ void decode_kernel(const DecodeParams p) {
 
   RowState rs{-INFINITY, -INFINITY, 0.f};
 
-  // Softmax of one step in 17 pieces that the caller interleaves with MFMAs (piece 0 must
-  // come at least 24 wait states after the last MFMA that wrote t.sa / t.sb).  A tile that
-  // this wave does not own (past the chunk, or past the loop) is masked whole.
-  auto softmax_piece = [&](StepTile& t, int st, int piece) __attribute__((always_inline)) {
-    if (piece == 0) {
-      // mask the tail / causal positions: register r holds tile token 2 r + gg, visible
-      // while T0 + 2 r + gg <= lim, i.e. while r <= c
-      const int T0a = (t_begin + 2 * st) * kTile;
-      const int T0b = T0a + kTile;
-      const bool va = 2 * st < ntiles, vb = 2 * st + 1 < ntiles;
-      if (!va || T0a + kTile - 1 > lim_min) {
-        const int c = va ? (lim - T0a - gg) >> 1 : -1;
+  // ---- softmax pieces.  max_a / max_b find the row's step max (masking first when the step
+  // needs it) and the step exponent, exp_piece(k) turns scores 2k, 2k+1 of [a | b] into
+  // probabilities, hilo_piece(q) encodes probabilities 4q .. 4q+3 as hi and lo e4m3 bytes.
+  // Each piece ends in an empty asm that takes its results, so the compiler computes them
+  // where the caller placed the piece (between two MFMAs) instead of next to their use.
+  auto mask_tile = [&](f32x16& x, int ti) __attribute__((always_inline)) {
+    // register r holds tile token 2 r + gg, visible while T0 + 2 r + gg <= lim, i.e. r <= c
+    const int T0 = (t_begin + ti) * kTile;
+    int c = ti < ntiles ? (lim - T0 - gg) >> 1 : -1;
+    asm volatile("" : "+v"(c));  // keeps the compares inside the (rarely taken) masked branch
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r > c) t.sa[r] = -INFINITY;
-      }
-      if (!vb || T0b + kTile - 1 > lim_min) {
-        const int c = vb ? (lim - T0b - gg) >> 1 : -1;
+    for (int r = 0; r < 16; ++r) x[r] = r > c ? -INFINITY : x[r];
+  };
+  auto max_a = [&](Probs& t, int st, bool masked) __attribute__((always_inline)) {
+    if (masked) mask_tile(t.a, 2 * st);
+    float m = fmaxf(fmaxf(t.a[0], t.a[1]), t.a[2]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (r > c) t.sb[r] = -INFINITY;
-      }
-      float m = fmaxf(fmaxf(t.sa[0], t.sa[1]), t.sa[2]);
+    for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, t.a[r]), t.a[r + 1]);
+    t.mpart = fmaxf(m, t.a[15]);
+    asm volatile("" : "+v"(t.mpart));
+  };
+  auto max_b = [&](Probs& t, int st, bool masked) __attribute__((always_inline)) {
+    if (masked) mask_tile(t.b, 2 * st + 1);
+    float m = fmaxf(fmaxf(t.mpart, t.b[0]), t.b[1]);
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, t.sa[r]), t.sa[r + 1]);
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) m = fmaxf(fmaxf(m, t.sb[r]), t.sb[r + 1]);
-      m = fmaxf(m, t.sa[15]);
-      const f32x2 both = row_pair(m);
-      const float mx = fmaxf(both[0], both[1]) * c2;  // the row's max; c2 > 0
-      if (rs.mu == -INFINITY) rs.mu = mx;  // first step with a visible position
-      rs.m_true = fmaxf(rs.m_true, mx);
-      const float mref = rs.mu == -INFINITY ? 0.f : rs.mu;
-      const float ef = fminf(fmaxf(floorf(mx - mref), -126.0f), 127.0f);
-      t.ef = (int)ef;
-      t.off = mref + ef - kLog2PScale;
-    } else if (piece <= 8) {  // p = 2^(c2 s - off), in [0, 448); 0 where masked
-      const int q = piece - 1;  // values 4q .. 4q + 3 of [sa | sb]
-      float sum = q == 0 ? 0.f : t.psum;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (q < 4) {
-          t.sa[4 * q + r] = __builtin_amdgcn_exp2f(fmaf(t.sa[4 * q + r], c2, -t.off));
-          sum += t.sa[4 * q + r];
-        } else {
-          t.sb[4 * (q - 4) + r] = __builtin_amdgcn_exp2f(fmaf(t.sb[4 * (q - 4) + r], c2, -t.off));
-          sum += t.sb[4 * (q - 4) + r];
-        }
-      }
-      t.psum = sum;
-      if (q == 7) rs.l_run += ldexpf(sum, t.ef);
-    } else {  // pieces 9..16: P bytes 4q .. 4q+3 as hi and lo e4m3
-      const int q = piece - 9;
-      const f32x16& v = q < 4 ? t.sa : t.sb;
-      const int o = 4 * (q & 3);
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[o], v[o + 1], 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[o + 2], v[o + 3], w, true);
-      const f32x2 d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-      const f32x2 d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-      int w2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[o] - d01[0], v[o + 1] - d01[1], 0, false);
-      w2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[o + 2] - d23[0], v[o + 3] - d23[1], w2, true);
-      t.hi[q] = w;
-      t.lo[q] = w2;
+    for (int r = 2; r < 16; r += 2) m = fmaxf(fmaxf(m, t.b[r]), t.b[r + 1]);
+    const f32x2 both = row_pair(m);
+    t.mpart = fmaxf(both[0], both[1]) * c2;  // the row's max; c2 > 0
+    asm volatile("" : "+v"(t.mpart));
+  };
+  auto step_exponent = [&](Probs& t) __attribute__((always_inline)) {
+    const float mx = t.mpart;
+    if (rs.mu == -INFINITY) rs.mu = mx;  // first step with a visible position
+    rs.m_true = fmaxf(rs.m_true, mx);
+    const float mref = rs.mu == -INFINITY ? 0.f : rs.mu;
+    const float ef = fminf(fmaxf(floorf(mx - mref), -126.0f), 127.0f);
+    t.ef = (int)ef;
+    t.off = mref + ef - kLog2PScale;
+    asm volatile("" : "+v"(t.off), "+v"(t.ef));
+  };
+  auto exp_piece = [&](Probs& t, int k) __attribute__((always_inline)) {
+    // p = 2^(c2 s - off), in [0, 448); 0 where masked
+    float x0, x1;
+    if (k < 8) {
+      x0 = t.a[2 * k] = __builtin_amdgcn_exp2f(fmaf(t.a[2 * k], c2, -t.off));
+      x1 = t.a[2 * k + 1] = __builtin_amdgcn_exp2f(fmaf(t.a[2 * k + 1], c2, -t.off));
+    } else {
+      x0 = t.b[2 * k - 16] = __builtin_amdgcn_exp2f(fmaf(t.b[2 * k - 16], c2, -t.off));
+      x1 = t.b[2 * k - 15] = __builtin_amdgcn_exp2f(fmaf(t.b[2 * k - 15], c2, -t.off));
     }
+    t.psum = (k == 0 ? x0 : t.psum + x0) + x1;
+    asm volatile("" : "+v"(t.psum));
+    if (k == 15) rs.l_run += ldexpf(t.psum, t.ef);
+  };
+  auto hilo_piece = [&](const Probs& t, int q, PBytes& pb) __attribute__((always_inline)) {
+    const f32x16& v = q < 4 ? t.a : t.b;
+    const int o = 4 * (q & 3);
+    // the first conversion of each word writes its low half; the high half is written next,
+    // so the register's old contents are irrelevant (an empty asm names a free register)
+    int w, w2;
+    asm volatile("" : "=v"(w));
+    asm volatile("" : "=v"(w2));
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[o], v[o + 1], w, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[o + 2], v[o + 3], w, true);
+    const f32x2 d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    w2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[o] - d01[0], v[o + 1] - d01[1], w2, false);
+    w2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[o + 2] - d23[0], v[o + 3] - d23[1], w2, true);
+    asm volatile("" : "+v"(w), "+v"(w2));
+    pb.hi[q] = w;
+    pb.lo[q] = w2;
+  };
+  // The whole softmax of a step, not overlapped (first step of a pass).
+  auto softmax_all = [&](Probs& t, int st, StepP& out) __attribute__((always_inline)) {
+    max_a(t, st, st >= nplain);
+    max_b(t, st, st >= nplain);
+    step_exponent(t);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) exp_piece(t, k);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) hilo_piece(t, q, out.pb);
+    out.ef = t.ef;
   };
 
-  f32x16 o[16];
-  i32x8 phi, plo;  // P of the step whose PV comes next, and its per-row exponent
-  int ef = 0;
+  f32x16 o[16];  // O^T blocks: register r of block d = row wrow0 + n, column 32 d + tok_of(gg, r)
 
-  // O += [hi | lo] . V of step st over the 16 blocks of 32 value columns, one V fragment
-  // (64 tokens x 32 columns) per block shared by the hi and lo MFMAs.  With kNext, the
-  // next step's softmax fills the gaps between these MFMAs.
-  auto pv_step = [&](int st, StepTile& nx, auto with_next) __attribute__((always_inline)) {
+  // O^T += V^T . [hi | lo]^T of step st over the 16 blocks of 32 value columns, one V fragment
+  // (64 tokens x 32 columns) per block shared by the hi and lo MFMAs.  With kNext, the whole
+  // softmax of the next step's scores t fills the 32 gaps between these MFMAs, ending in its
+  // P bytes nx.
+  auto pv_step = [&](int st, const StepP& cur, Probs& t, StepP& nx, bool mask_next,
+                     auto with_next) __attribute__((always_inline)) {
     constexpr bool kNext = decltype(with_next)::value;
     const uint32_t sb = step_base(st);
-    const int escale = 127 + ef;
+    const int escale = 127 + cur.ef;
     i32x2 va[16][4];
 #pragma unroll
     for (int d = 0; d < kVAhead; ++d) {
@@ -408,6 +491,18 @@ void decode_kernel(const DecodeParams p) {
       va[d][2] = lds_read_tr8(lds, sb + kSlot + vrow0 + 32 * d);
       va[d][3] = lds_read_tr8(lds, sb + kSlot + vrow1 + 32 * d);
     }
+    // gap g (after PV MFMA g): 0 max_a, 1 max_b, 2 exponent, 3..18 exp pieces, 19..26 hi/lo
+    auto gap = [&](int g) __attribute__((always_inline)) {
+      if constexpr (kNext) {
+        sched_fence();
+        if (g == 0) max_a(t, st + 1, mask_next);  // 2 MFMAs after the last one that wrote t.a
+        else if (g == 1) max_b(t, st + 1, mask_next);  // 2 MFMAs after the last write of t.b
+        else if (g == 2) step_exponent(t);
+        else if (g <= 18) exp_piece(t, g - 3);
+        else if (g <= 26) hilo_piece(t, g - 19, nx.pb);
+        sched_fence();
+      }
+    };
 #pragma unroll
     for (int d = 0; d < 16; ++d) {
       if (d + kVAhead < 16) {
@@ -417,24 +512,67 @@ void decode_kernel(const DecodeParams p) {
         va[e][2] = lds_read_tr8(lds, sb + kSlot + vrow0 + 32 * e);
         va[e][3] = lds_read_tr8(lds, sb + kSlot + vrow1 + 32 * e);
       }
-      const i32x8 vb = (i32x8){va[d][0][0], va[d][0][1], va[d][1][0], va[d][1][1],
-                               va[d][2][0], va[d][2][1], va[d][3][0], va[d][3][1]};
-      mfma_pv(o[d], phi, vb, escale);
-      if constexpr (kNext) {
-        sched_fence();
-        if (d == 0) mfma_drain2(nx.sa, nx.sb);  // the QK chains' results are read from here
-        if (2 * d < 17) softmax_piece(nx, st + 1, 2 * d);
-        sched_fence();
-      }
-      mfma_pv(o[d], plo, vb, escale);
-      if constexpr (kNext) {
-        if (2 * d + 1 < 17) {
-          sched_fence();
-          softmax_piece(nx, st + 1, 2 * d + 1);
-          sched_fence();
-        }
-      }
+      VFrag vf;
+      vf.h[0] = va[d][0];
+      vf.h[1] = va[d][1];
+      vf.h[2] = va[d][2];
+      vf.h[3] = va[d][3];
+      const i32x8 vb = vf.v;
+      mfma_pv(o[d], vb, cur.pb.hi, escale);
+      gap(2 * d);
+      mfma_pv(o[d], vb, cur.pb.lo, escale);
+      gap(2 * d + 1);
     }
+    if constexpr (kNext) nx.ef = t.ef;
+  };
+
+  // Steady-state step st: QK of step st + 1 (with the DMA of step st + 3 between its MFMAs),
+  // then P.V of step st (with the softmax of step st + 1 between its MFMAs).
+  StepPages sp_next;  // pages of the next step to issue
+  auto iteration = [&](int st, const StepP& cur, StepP& nx) __attribute__((always_inline)) {
+    Probs t;
+    const uint32_t sb1 = step_base(st + 1);
+    KPair kp[9];
+#pragma unroll
+    for (int c = 0; c < kKAhead; ++c) kp[c] = read_kpair(sb1, c);
+    // the DMA of step st + 3 goes into the slot that step st - 1 left: resources in gaps 0
+    // and 4, two DMA instructions per gap after that
+    const uint32_t slot3 = slot_of(st + 3);
+    __amdgpu_buffer_rsrc_t ra, rb;
+    auto dma_gap = [&](int g) __attribute__((always_inline)) {
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      using I4 = std::integral_constant<int, 4>;
+      sched_fence();
+      if (g == 0) ra = tile_rsrc(2 * (st + 3), sp_next.page_a, sp_next.po_a);
+      if (g == 1) { tile_dma(ra, slot3, I0{}, I0{}); tile_dma(ra, slot3, I0{}, I1{}); }
+      if (g == 2) { tile_dma(ra, slot3, I0{}, I2{}); tile_dma(ra, slot3, I0{}, I3{}); }
+      if (g == 3) tile_dma(ra, slot3, I0{}, I4{});
+      if (g == 4) rb = tile_rsrc(2 * (st + 3) + 1, sp_next.page_b, sp_next.po_b);
+      if (g == 5) { tile_dma(rb, slot3, I1{}, I0{}); tile_dma(rb, slot3, I1{}, I1{}); }
+      if (g == 6) { tile_dma(rb, slot3, I1{}, I2{}); tile_dma(rb, slot3, I1{}, I3{}); }
+      if (g == 7) tile_dma(rb, slot3, I1{}, I4{});
+      sched_fence();
+    };
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+      if (c + kKAhead < 9) kp[c + kKAhead] = read_kpair(sb1, c + kKAhead);
+      if (c == 0) t.a = mfma_qk_first(cat8(kp[0].a0, kp[0].a1), qf[0]);
+      else mfma_qk(t.a, cat8(kp[c].a0, kp[c].a1), qf[c]);
+      dma_gap(2 * c);
+      if (c == 0) t.b = mfma_qk_first(cat8(kp[0].b0, kp[0].b1), qf[0]);
+      else mfma_qk(t.b, cat8(kp[c].b0, kp[c].b1), qf[c]);
+      dma_gap(2 * c + 1);
+    }
+    pv_step(st, cur, t, nx, st + 1 >= nplain, std::true_type{});
+    // pages of step st + 4 (scalar loads, waited for after the barrier where no LDS read is
+    // outstanding); step st + 2 landed for every wave and every wave is past step st
+    sp_next = next_pages();
+    wait_vmcnt<kLmin>();
+    __syncthreads();
+    asm volatile("" ::"s"(sp_next.page_a), "s"(sp_next.page_b));
   };
 
 #pragma unroll 1
@@ -442,10 +580,15 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int d = 0; d < 16; ++d) o[d] = (f32x16){0.f};
     rs.l_run = 0.f;
+    cur_pe = t_begin / tpp;
+    cur_po = t_begin - cur_pe * tpp;
 
     // ---- stage the workgroup's 128 query rows (contiguous in q8) in tile slots 4..7 with
     // steps 0 and 1 in flight beside them.  Each pass stages them again, so the Q fragments
     // are live within a pass only.
+    const StepPages sp0 = next_pages();
+    const StepPages sp1 = next_pages();
+    const StepPages sp2 = next_pages();
     {
       const int qrows = min(kRows, M - row0);
       const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -456,8 +599,8 @@ void decode_kernel(const DecodeParams p) {
       for (int j = 0; j < kQDma / 4; ++j)
         dma16_s(wave_lds, qvoff + 4096u * j, qrsrc, kQSlot * kSlot + 4096 * j);
     }
-    issue_step(0, page_of(0), page_of(1));
-    issue_step(1, page_of(2), page_of(3));
+    issue_step(0, sp0);
+    issue_step(1, sp1);
     wait_vmcnt<2 * kLmin>();  // this wave's Q chunks have landed
     __syncthreads();
     {
@@ -467,70 +610,49 @@ void decode_kernel(const DecodeParams p) {
         qf[c] = cat8(lds_read16(lds, qrow + 64 * c), lds_read16(lds, qrow + 64 * c + 16));
     }
     __syncthreads();  // the Q slots are free from here on
-    issue_step(2, page_of(4), page_of(5));
+    issue_step(2, sp2);
+    sp_next = next_pages();  // step 3
 
-    // ---- step 0: scores and probabilities, not overlapped with anything
+    // ---- step 0: scores and P bytes, not overlapped with anything
     wait_vmcnt<2 * kLmin>();
     __syncthreads();
+    StepP X, Y;
     {
-      StepTile t;
+      Probs t;
       const uint32_t sb = step_base(0);
 #pragma unroll
       for (int c = 0; c < 9; ++c) {
         const KPair k = read_kpair(sb, c);
         if (c == 0) {
-          t.sa = mfma_qk_first(cat8(k.a0, k.a1), qf[0]);
-          t.sb = mfma_qk_first(cat8(k.b0, k.b1), qf[0]);
+          t.a = mfma_qk_first(cat8(k.a0, k.a1), qf[0]);
+          t.b = mfma_qk_first(cat8(k.b0, k.b1), qf[0]);
         } else {
-          mfma_qk(t.sa, cat8(k.a0, k.a1), qf[c]);
-          mfma_qk(t.sb, cat8(k.b0, k.b1), qf[c]);
+          mfma_qk(t.a, cat8(k.a0, k.a1), qf[c]);
+          mfma_qk(t.b, cat8(k.b0, k.b1), qf[c]);
         }
       }
-      mfma_drain2(t.sa, t.sb);
-#pragma unroll
-      for (int piece = 0; piece < 17; ++piece) softmax_piece(t, 0, piece);
-      phi = t.hi;
-      plo = t.lo;
-      ef = t.ef;
+      mfma_drain2(t.a, t.b);
+      softmax_all(t, 0, X);
     }
     // step 1 visible to every wave before the loop reads it
     wait_vmcnt<kLmin>();
     __syncthreads();
-    int pg0 = page_of(6), pg1 = page_of(7);  // pages of the next step to issue (3)
 
-    for (int st = 0; st + 1 < nsteps; ++st) {
-      // step st + 1 is visible and step slot (st - 1) % 4 is free: barrier at the end of the
-      // previous iteration, or just above
-      StepTile t;
-      const uint32_t sb1 = step_base(st + 1);
-      KPair kp[9];
-#pragma unroll
-      for (int c = 0; c < kKAhead; ++c) kp[c] = read_kpair(sb1, c);
-#pragma unroll
-      for (int c = 0; c < 9; ++c) {
-        if (c + kKAhead < 9) kp[c + kKAhead] = read_kpair(sb1, c + kKAhead);
-        if (c == 0) {
-          t.sa = mfma_qk_first(cat8(kp[0].a0, kp[0].a1), qf[0]);
-          t.sb = mfma_qk_first(cat8(kp[0].b0, kp[0].b1), qf[0]);
-        } else {
-          mfma_qk(t.sa, cat8(kp[c].a0, kp[c].a1), qf[c]);
-          mfma_qk(t.sb, cat8(kp[c].b0, kp[c].b1), qf[c]);
-        }
-        if (c == 1) issue_step(st + 3, pg0, pg1);  // into the slot that step st - 1 left
-      }
-      pv_step(st, t, std::true_type{});
-      phi = t.hi;
-      plo = t.lo;
-      ef = t.ef;
-      // step st + 2 landed for every wave, and every wave is past its reads of step st
-      wait_vmcnt<kLmin>();
-      __syncthreads();
-      pg0 = page_of(2 * (st + 4));
-      pg1 = page_of(2 * (st + 4) + 1);
+    // two steps per trip, the P buffers X and Y trading roles
+    int st = 0;
+    for (; st + 2 < nsteps; st += 2) {
+      iteration(st, X, Y);
+      iteration(st + 1, Y, X);
+    }
+    if (st + 1 < nsteps) {
+      iteration(st, X, Y);
+      ++st;
+      X = Y;
     }
     {
-      StepTile unused;
-      pv_step(nsteps - 1, unused, std::false_type{});  // landed before the last barrier
+      Probs unused_t;
+      StepP unused_p;
+      pv_step(st, X, unused_t, unused_p, false, std::false_type{});  // the last step
     }
     mfma_drain_acc(o[15]);
 #pragma unroll
@@ -548,33 +670,20 @@ void decode_kernel(const DecodeParams p) {
   const f32x2 lpair = row_pair(rs.l_run);
   const float Ls = lpair[0] + lpair[1];  // both halves of the row
   const float f = (mu != -INFINITY && Ls > 0.f) ? 1.0f / Ls : 0.f;
-  if (lane < 32 && row_ok)
+  if (!row_ok) return;
+  if (lane < 32)
     p.partial_lse[prow + R] = Ls > 0.f ? (mu + log2f(Ls) - kLog2PScale) * kLn2 : -INFINITY;
-
-  // per-register factors: register r of every block holds row 8(r/4) + 4gg + r%4, i.e. the
-  // factor of lane tok_of(gg, r) (lanes n and n + 32 hold the same value)
-  float fr[16];
+  // registers 4k .. 4k+3 of block d: columns 32 d + 8 k + 4 gg + 0..3 of row R
+  uint2* wout = (uint2*)((_Float16*)p.partial_o + (prow + R) * kDv + 4 * gg);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) fr[r] = __shfl(f, tok_of(gg, r));
-
-  // register r of block d is row wrow0 + tok_of(gg, r), column 32 d + n
-  _Float16* wout = (_Float16*)p.partial_o + (prow + wrow0) * kDv + n;
-  if (wrow0 + 32 <= M) {
+  for (int d = 0; d < 16; ++d) {
+    const f32x16 v = from_acc(o[d]);
 #pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      const f32x16 v = from_acc(o[d]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        wout[tok_of(gg, r) * kDv + 32 * d] = (_Float16)(v[r] * fr[r]);
-    }
-  } else {
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      const f32x16 v = from_acc(o[d]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (wrow0 + tok_of(gg, r) < M)
-          wout[tok_of(gg, r) * kDv + 32 * d] = (_Float16)(v[r] * fr[r]);
+    for (int k = 0; k < 4; ++k) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      const h4 h = {(_Float16)(v[4 * k] * f), (_Float16)(v[4 * k + 1] * f),
+                    (_Float16)(v[4 * k + 2] * f), (_Float16)(v[4 * k + 3] * f)};
+      wout[(32 * d + 8 * k) / 4] = __builtin_bit_cast(uint2, h);
     }
   }
 }

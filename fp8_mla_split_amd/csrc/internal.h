@@ -20,6 +20,7 @@ struct DecodeParams {
   float* partial_lse;
   int batch, q_tokens, heads, rows;   // rows = q_tokens * heads
   int page_size, max_pages, num_splits, groups;
+  int64_t page_bytes;                 // page_size * 576
   float c2;                           // q_scale * kv_scale * softmax_scale * log2(e)
   float kv_scale;
 };

@@ -158,6 +158,7 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   p.heads = heads;
   p.rows = (int)M;
   p.page_size = page_size;
+  p.page_bytes = (int64_t)page_size * mla::kD;
   p.max_pages = max_pages;
   p.num_splits = S;
   p.groups = (int)groups;

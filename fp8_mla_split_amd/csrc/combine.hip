@@ -3,24 +3,29 @@
 // The faster split-KV reduction item of the MLA section of the arex-research.com Vera Rubin /
 // Kimi K3 write-up replaces a merge that loaded one partial, waited for it, then loaded the
 // next (one cache latency per partial) by one that issues every partial's load first and then
-// accumulates from registers.  Here one workgroup (four waves) owns one output row; each lane
-// owns 8 of its 512 value columns, and wave w takes the splits s = w, w + 4, ...  A wave reads
-// the row's S log-sum-exps, then, in batches of 16 splits, issues all 16 partial-row loads
-// (16 bytes per lane, one 1 KiB row per instruction) before it touches any of them.  The
-// four waves' sums meet in LDS.
+// accumulates from registers.  Here a row's 512 value columns are split over kCw workgroups
+// (kCw * rows workgroups in all, so a batch-1 merge still spreads over the whole chip); a
+// workgroup has NW = ceil(S / (16 kCw)) waves (at most 16) and each wave owns 16 kCw splits
+// per batch.  A lane covers 8 columns (16 bytes) of one split row, so one wave-wide load
+// instruction fetches kCw split rows; a wave issues its whole batch of 16 loads (and the 16
+// log-sum-exps) before it touches any of them, keeps a running max of its splits' lse and
+// rescales as it goes, and the workgroup's lanes meet in LDS at the end.
 //
 //   M = max_s lse_s;  w_s = exp(lse_s - M);  O = v_scale * sum_s w_s O_s / sum_s w_s;
 //   lse = M + log sum_s w_s
 //
 // Partial rows are fp16 values in units of v_scale.  Splits whose lse is -inf contribute
-// nothing and their partial rows are never read (their memory may hold anything).
-// Memory-bound: B*S*R*(1024 + 4) bytes read.
+// nothing (their partial rows may hold anything; they are loaded but never used).
+// Memory-bound: B*S*R*(1024 + 4) bytes read, B*R*1024 (+ 4) written.
 #include "internal.h"
 
 namespace mla {
 namespace {
 
-constexpr int kBatch = 16;  // partial rows in flight per wave
+constexpr int kBatch = 16;   // load instructions in flight per wave
+constexpr int kCw = 2;       // workgroups (column chunks) per output row
+constexpr int kLanesPerRow = 64 / kCw;  // lanes covering one split row's chunk
+constexpr int kMaxWaves = 16;
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -29,71 +34,82 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
+struct Partial {
+  float m, ws;
+  float acc[8];
+};
 
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ po,
-                                                      const float* __restrict__ pl, int S, int R,
-                                                      float v_scale, uint16_t* __restrict__ out,
-                                                      float* __restrict__ out_lse) {
-  __shared__ float red_m[4];
-  __shared__ float red_w[4];
-  __shared__ float4 red_o[4][64][2];
-  const int row = blockIdx.x;  // b * R + r
+__global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
+    const uint16_t* __restrict__ po, const float* __restrict__ pl, int S, int R, float v_scale,
+    uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+  __shared__ Partial red[kMaxWaves * 64];
+  const int row = blockIdx.x / kCw;  // b * R + r
+  const int chunk = blockIdx.x - row * kCw;
   const int b = row / R, r = row - b * R;
+  const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane / kLanesPerRow;             // which of the kCw split rows of a load
+  const int pos = lane - sub * kLanesPerRow;       // 16-byte column group within the chunk
+  const int col0 = chunk * (kDv / kCw) + 8 * pos;  // first of this lane's 8 columns
 
-  const float* lse = pl + (int64_t)b * S * R + r;                       // stride R over splits
-  const uint16_t* o = po + ((int64_t)b * S * R + r) * kDv + 8 * lane;   // stride R*512
+  const float* lse = pl + (int64_t)b * S * R + r;                      // stride R over splits
+  const uint16_t* o = po + ((int64_t)b * S * R + r) * kDv + col0;      // stride R*512
   const int64_t ostride = (int64_t)R * kDv;
 
-  // row max of the lse over all splits
-  float m = -INFINITY;
-  for (int s = threadIdx.x; s < S; s += 256) m = fmaxf(m, lse[(int64_t)s * R]);
-  m = wave_max(m);
-  if (lane == 0) red_m[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (m != -INFINITY) {
-    for (int s0 = wave; s0 < S; s0 += 4 * kBatch) {
-      uint4 v[kBatch];
-      float w[kBatch];
+  Partial p;
+  p.m = -INFINITY;
+  p.ws = 0.f;
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {  // issue every load of the batch first
-        const int s = min(s0 + 4 * j, S - 1);
-        w[j] = s0 + 4 * j < S ? lse[(int64_t)s * R] : -INFINITY;
-        v[j] = *(const uint4*)(o + (int64_t)s * ostride);
-      }
+  for (int c = 0; c < 8; ++c) p.acc[c] = 0.f;
+
+  // split of load j of batch t: ((t * nw + wave) * kBatch + j) * kCw + sub
+  for (int s0 = wave * kBatch * kCw; s0 < S; s0 += nw * kBatch * kCw) {
+    uint4 v[kBatch];
+    float l[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {  // every load of the batch first
+      const int s = s0 + j * kCw + sub;
+      const int sc = min(s, S - 1);
+      l[j] = s < S ? lse[(int64_t)sc * R] : -INFINITY;
+      v[j] = *(const uint4*)(o + (int64_t)sc * ostride);
+    }
+    float bm = p.m;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, l[j]);
+    if (bm != -INFINITY) {
+      const float rescale = __expf(p.m - bm);  // 0 when p.m is -inf
+      p.ws *= rescale;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) p.acc[c] *= rescale;
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {  // then accumulate from registers
-        if (w[j] == -INFINITY) continue;  // wave-uniform: an empty split is never read
-        const float e = __expf(w[j] - m);
-        wsum += e;
+        const bool live = l[j] != -INFINITY;
+        const float e = live ? __expf(l[j] - bm) : 0.f;
+        p.ws += e;
         const _Float16* h = (const _Float16*)&v[j];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = fmaf(e, (float)h[c], acc[c]);
+        for (int c = 0; c < 8; ++c) p.acc[c] = fmaf(e, live ? (float)h[c] : 0.f, p.acc[c]);
       }
+      p.m = bm;
     }
   }
-  red_o[wave][lane][0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  red_o[wave][lane][1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-  if (lane == 0) red_w[wave] = wsum;
+  red[threadIdx.x] = p;
   __syncthreads();
-  if (wave != 0) return;
-  float tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float ws = 0.f;
+  if (wave != 0 || sub != 0) return;
+
+  // lane pos of wave 0 merges the nw * kCw partials of its column group
+  float M = -INFINITY;
+  for (int k = 0; k < nw * kCw; ++k)
+    M = fmaxf(M, red[(k / kCw) * 64 + (k % kCw) * kLanesPerRow + pos].m);
+  float ws = 0.f, tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    for (int k = 0; k < nw * kCw; ++k) {
+      const Partial& q = red[(k / kCw) * 64 + (k % kCw) * kLanesPerRow + pos];
+      const float sc = __expf(q.m - M);  // 0 for a partial that saw no live split
+      ws += sc * q.ws;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float4 a = red_o[k][lane][0], c = red_o[k][lane][1];
-    tot[0] += a.x; tot[1] += a.y; tot[2] += a.z; tot[3] += a.w;
-    tot[4] += c.x; tot[5] += c.y; tot[6] += c.z; tot[7] += c.w;
-    ws += red_w[k];
+      for (int c = 0; c < 8; ++c) tot[c] = fmaf(sc, q.acc[c], tot[c]);
+    }
   }
   const float f = ws > 0.f ? v_scale / ws : 0.f;
   uint4 packed;
@@ -101,16 +117,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   packed.y = (uint32_t)bf16_rne(tot[2] * f) | ((uint32_t)bf16_rne(tot[3] * f) << 16);
   packed.z = (uint32_t)bf16_rne(tot[4] * f) | ((uint32_t)bf16_rne(tot[5] * f) << 16);
   packed.w = (uint32_t)bf16_rne(tot[6] * f) | ((uint32_t)bf16_rne(tot[7] * f) << 16);
-  *(uint4*)(out + (int64_t)row * kDv + 8 * lane) = packed;
-  if (out_lse != nullptr && lane == 0) out_lse[row] = ws > 0.f ? m + logf(ws) : -INFINITY;
+  *(uint4*)(out + (int64_t)row * kDv + col0) = packed;
+  if (out_lse != nullptr && chunk == 0 && pos == 0)
+    out_lse[row] = ws > 0.f ? M + logf(ws) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
                           float v_scale, uint16_t* out, float* out_lse, hipStream_t s) {
-  const int64_t blocks = (int64_t)batch * rows;
-  combine_kernel<<<(unsigned)blocks, 256, 0, s>>>(po, pl, splits, rows, v_scale, out, out_lse);
+  const int64_t blocks = (int64_t)batch * rows * kCw;
+  int nw = (splits + kBatch * kCw - 1) / (kBatch * kCw);
+  nw = nw < 1 ? 1 : (nw > kMaxWaves ? kMaxWaves : nw);
+  combine_kernel<<<(unsigned)blocks, 64 * nw, 0, s>>>(po, pl, splits, rows, v_scale, out,
+                                                       out_lse);
   return hipGetLastError();
 }
 

@@ -118,8 +118,8 @@ __device__ __forceinline__ void dma16_s(uint32_t lds_addr, uint32_t voff,
 // AGPRs (left to itself the compiler puts every accumulator in AGPRs, which then do not
 // hold O).  The "memory" clobber keeps the LDS fragment reads where the source places them.
 // Hazards the compiler cannot see through the asm are handled here: the QK operands come
-// straight from LDS reads (ordered by s_waitcnt, no VALU producer), the PV MFMAs take a
-// VALU-written scale and P bytes and wait two states first; a non-MFMA reader of an MFMA
+// straight from LDS reads (ordered by s_waitcnt, no VALU producer), a PV MFMA waits two
+// states where its VALU-written scale may be fresh (see mfma_pv); a non-MFMA reader of an MFMA
 // result is placed at least two MFMAs (128 clocks) after it or behind an explicit drain
 // that takes the accumulators as operands (the compiler treats an asm output as ready at
 // once and would otherwise copy it straight after the MFMA).
@@ -138,12 +138,21 @@ __device__ __forceinline__ void mfma_qk(f32x16& d, const i32x8& a, const i32x8& 
                : "memory");
 }
 // acc (O^T block) += V^T . P^T: A = V fragment (scale 2^0), B = P bytes (scale 2^(sb-127)).
+// The first of a step waits two states for its freshly computed scale; the later ones read
+// registers written long before.
+template <bool kFirst>
 __device__ __forceinline__ void mfma_pv(f32x16& acc, const i32x8& v, const i32x8& pbytes,
                                         int scale_b) {
-  asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
-               : "+a"(acc)
-               : "v"(v), "v"(pbytes), "v"(127), "v"(scale_b)
-               : "memory");
+  if constexpr (kFirst)
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(acc)
+                 : "v"(v), "v"(pbytes), "v"(127), "v"(scale_b)
+                 : "memory");
+  else
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(acc)
+                 : "v"(v), "v"(pbytes), "v"(127), "v"(scale_b)
+                 : "memory");
 }
 __device__ __forceinline__ void mfma_drain2(f32x16& a, f32x16& b) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
@@ -220,9 +229,12 @@ struct PBytes {
   i32x8 hi, lo;
 };
 
-// What the P.V of a step needs: its P bytes and exponent.
+// What the P.V of a step needs: its P bytes and exponent.  The bytes of tile a are encoded
+// one phase later than those of tile b (between the next step's QK MFMAs), so tile a's
+// probabilities travel along until then.
 struct StepP {
   PBytes pb;
+  f32x16 pa;
   int ef;
 };
 
@@ -442,8 +454,7 @@ void decode_kernel(const DecodeParams p) {
     asm volatile("" : "+v"(t.psum));
     if (k == 15) rs.l_run += ldexpf(t.psum, t.ef);
   };
-  auto hilo_piece = [&](const Probs& t, int q, PBytes& pb) __attribute__((always_inline)) {
-    const f32x16& v = q < 4 ? t.a : t.b;
+  auto hilo_piece = [&](const f32x16& v, int q, PBytes& pb) __attribute__((always_inline)) {
     const int o = 4 * (q & 3);
     // the first conversion of each word writes its low half; the high half is written next,
     // so the register's old contents are irrelevant (an empty asm names a free register)
@@ -468,7 +479,8 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) exp_piece(t, k);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) hilo_piece(t, q, out.pb);
+    for (int q = 4; q < 8; ++q) hilo_piece(t.b, q, out.pb);
+    out.pa = t.a;
     out.ef = t.ef;
   };
 
@@ -491,7 +503,8 @@ void decode_kernel(const DecodeParams p) {
       va[d][2] = lds_read_tr8(lds, sb + kSlot + vrow0 + 32 * d);
       va[d][3] = lds_read_tr8(lds, sb + kSlot + vrow1 + 32 * d);
     }
-    // gap g (after PV MFMA g): 0 max_a, 1 max_b, 2 exponent, 3..18 exp pieces, 19..26 hi/lo
+    // gap g (after PV MFMA g): 0 max_a, 1 max_b, 2 exponent, 3..18 exp pieces, 20, 22, 24,
+    // 26 hi/lo of tile b
     auto gap = [&](int g) __attribute__((always_inline)) {
       if constexpr (kNext) {
         sched_fence();
@@ -499,7 +512,7 @@ void decode_kernel(const DecodeParams p) {
         else if (g == 1) max_b(t, st + 1, mask_next);  // 2 MFMAs after the last write of t.b
         else if (g == 2) step_exponent(t);
         else if (g <= 18) exp_piece(t, g - 3);
-        else if (g <= 26) hilo_piece(t, g - 19, nx.pb);
+        else if (g >= 20 && g <= 26 && g % 2 == 0) hilo_piece(t.b, 4 + (g - 20) / 2, nx.pb);
         sched_fence();
       }
     };
@@ -518,18 +531,22 @@ void decode_kernel(const DecodeParams p) {
       vf.h[2] = va[d][2];
       vf.h[3] = va[d][3];
       const i32x8 vb = vf.v;
-      mfma_pv(o[d], vb, cur.pb.hi, escale);
+      if (d == 0) mfma_pv<true>(o[d], vb, cur.pb.hi, escale);
+      else mfma_pv<false>(o[d], vb, cur.pb.hi, escale);
       gap(2 * d);
-      mfma_pv(o[d], vb, cur.pb.lo, escale);
+      mfma_pv<false>(o[d], vb, cur.pb.lo, escale);
       gap(2 * d + 1);
     }
-    if constexpr (kNext) nx.ef = t.ef;
+    if constexpr (kNext) {
+      nx.ef = t.ef;
+      nx.pa = t.a;
+    }
   };
 
   // Steady-state step st: QK of step st + 1 (with the DMA of step st + 3 between its MFMAs),
   // then P.V of step st (with the softmax of step st + 1 between its MFMAs).
   StepPages sp_next;  // pages of the next step to issue
-  auto iteration = [&](int st, const StepP& cur, StepP& nx) __attribute__((always_inline)) {
+  auto iteration = [&](int st, StepP& cur, StepP& nx) __attribute__((always_inline)) {
     Probs t;
     const uint32_t sb1 = step_base(st + 1);
     KPair kp[9];
@@ -554,6 +571,7 @@ void decode_kernel(const DecodeParams p) {
       if (g == 5) { tile_dma(rb, slot3, I1{}, I0{}); tile_dma(rb, slot3, I1{}, I1{}); }
       if (g == 6) { tile_dma(rb, slot3, I1{}, I2{}); tile_dma(rb, slot3, I1{}, I3{}); }
       if (g == 7) tile_dma(rb, slot3, I1{}, I4{});
+      if (g >= 9 && g <= 15 && g % 2 == 1) hilo_piece(cur.pa, (g - 9) / 2, cur.pb);  // tile a
       sched_fence();
     };
 #pragma unroll
@@ -650,6 +668,8 @@ void decode_kernel(const DecodeParams p) {
       X = Y;
     }
     {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hilo_piece(X.pa, q, X.pb);
       Probs unused_t;
       StepP unused_p;
       pv_step(st, X, unused_t, unused_p, false, std::false_type{});  // the last step
@@ -670,11 +690,14 @@ void decode_kernel(const DecodeParams p) {
   const f32x2 lpair = row_pair(rs.l_run);
   const float Ls = lpair[0] + lpair[1];  // both halves of the row
   const float f = (mu != -INFINITY && Ls > 0.f) ? 1.0f / Ls : 0.f;
-  if (!row_ok) return;
-  if (lane < 32)
+  if (lane < 32 && row_ok)
     p.partial_lse[prow + R] = Ls > 0.f ? (mu + log2f(Ls) - kLog2PScale) * kLn2 : -INFINITY;
-  // registers 4k .. 4k+3 of block d: columns 32 d + 8 k + 4 gg + 0..3 of row R
-  uint2* wout = (uint2*)((_Float16*)p.partial_o + (prow + R) * kDv + 4 * gg);
+  // Transpose through LDS (free now: every DMA has landed and every wave is past the ring) so
+  // that each store instruction writes one whole 1 KiB partial row: this wave's 32 rows x 512
+  // columns go to LDS rows of kOPitch bytes (registers 4k .. 4k+3 of block d hold columns
+  // 32 d + 8 k + 4 gg + 0..3 of row n), then lane l stores columns 8 l .. 8 l + 7 of a row.
+  constexpr int kOPitch = 1040;  // 16-byte aligned; 2-way bank conflicts on the 8-byte writes
+  uint8_t* ob = lds + wave * (32 * kOPitch);
 #pragma unroll
   for (int d = 0; d < 16; ++d) {
     const f32x16 v = from_acc(o[d]);
@@ -683,9 +706,14 @@ void decode_kernel(const DecodeParams p) {
       typedef _Float16 h4 __attribute__((ext_vector_type(4)));
       const h4 h = {(_Float16)(v[4 * k] * f), (_Float16)(v[4 * k + 1] * f),
                     (_Float16)(v[4 * k + 2] * f), (_Float16)(v[4 * k + 3] * f)};
-      wout[(32 * d + 8 * k) / 4] = __builtin_bit_cast(uint2, h);
+      *(uint2*)(ob + n * kOPitch + 2 * (32 * d + 8 * k + 4 * gg)) = __builtin_bit_cast(uint2, h);
     }
   }
+  _Float16* orow = (_Float16*)p.partial_o + (prow + wrow0) * kDv + 8 * lane;
+  const int nrows = min(32, M - wrow0);
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+    if (r < nrows) *(uint4*)(orow + r * kDv) = *(const uint4*)(ob + r * kOPitch + 16 * lane);
 }
 
 }  // namespace

@@ -59,6 +59,7 @@
 // last PV MFMA, so the matrix pipe keeps working through it.  Masking (sequence tail,
 // causal positions, tiles past the chunk) is a uniform branch taken only in the last steps.
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -229,14 +230,32 @@ struct PBytes {
   i32x8 hi, lo;
 };
 
-// What the P.V of a step needs: its P bytes and exponent.  The bytes of tile a are encoded
-// one phase later than those of tile b (between the next step's QK MFMAs), so tile a's
-// probabilities travel along until then.
+// What the P.V of a step needs: its P bytes and exponent.
 struct StepP {
   PBytes pb;
-  f32x16 pa;
   int ef;
 };
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1 in order, so every index in
+// the body is a compile-time constant (a #pragma unroll of a large body is not guaranteed).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Position of MFMA slot s of a pipeline stage among the MFMAs the stage issues: slots run
+// (QK, PV hi, PV lo) x 16, QK, QK; a stage without QK or without PV skips those slots.
+__host__ __device__ constexpr bool slot_is_qk(int s) { return s >= 48 || s % 3 == 0; }
+__host__ __device__ constexpr int slot_gap(int s, bool qk, bool pv) {
+  int g = -1;
+  for (int t = 0; t <= s; ++t)
+    if (slot_is_qk(t) ? qk : pv) ++g;
+  return g;
+}
 
 // K fragments of one QK MFMA pair (tile a, tile b).
 struct KPair {
@@ -402,7 +421,7 @@ void decode_kernel(const DecodeParams p) {
 
   // ---- softmax pieces.  max_a / max_b find the row's step max (masking first when the step
   // needs it) and the step exponent, exp_piece(k) turns scores 2k, 2k+1 of [a | b] into
-  // probabilities, hilo_piece(q) encodes probabilities 4q .. 4q+3 as hi and lo e4m3 bytes.
+  // probabilities, hilo_pair encodes two probabilities as hi and lo e4m3 bytes.
   // Each piece ends in an empty asm that takes its results, so the compiler computes them
   // where the caller placed the piece (between two MFMAs) instead of next to their use.
   auto mask_tile = [&](f32x16& x, int ti) __attribute__((always_inline)) {
@@ -454,143 +473,169 @@ void decode_kernel(const DecodeParams p) {
     asm volatile("" : "+v"(t.psum));
     if (k == 15) rs.l_run += ldexpf(t.psum, t.ef);
   };
-  auto hilo_piece = [&](const f32x16& v, int q, PBytes& pb) __attribute__((always_inline)) {
-    const int o = 4 * (q & 3);
-    // the first conversion of each word writes its low half; the high half is written next,
-    // so the register's old contents are irrelevant (an empty asm names a free register)
-    int w, w2;
-    asm volatile("" : "=v"(w));
-    asm volatile("" : "=v"(w2));
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[o], v[o + 1], w, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[o + 2], v[o + 3], w, true);
-    const f32x2 d01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    const f32x2 d23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-    w2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[o] - d01[0], v[o + 1] - d01[1], w2, false);
-    w2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[o + 2] - d23[0], v[o + 3] - d23[1], w2, true);
-    asm volatile("" : "+v"(w), "+v"(w2));
+  // hi/lo bytes of probabilities o, o + 1 of tile v, which fill half (high or low) of word q of
+  // the step's P bytes.  The low half comes first and starts the word in a free register (an
+  // empty asm names it; its old contents are overwritten by the high half next).
+  auto hilo_pair = [&](const f32x16& v, int o, int q, auto hc, PBytes& pb)
+      __attribute__((always_inline)) {
+    constexpr bool high = decltype(hc)::value;
+    int w = pb.hi[q], w2 = pb.lo[q];
+    if (!high) {
+      asm volatile("" : "=v"(w));
+      asm volatile("" : "=v"(w2));
+    }
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[o], v[o + 1], w, high);
+    const f32x2 dh = __builtin_amdgcn_cvt_pk_f32_fp8(w, high);
+    w2 = __builtin_amdgcn_cvt_pk_fp8_f32(v[o] - dh[0], v[o + 1] - dh[1], w2, high);
+    asm volatile("" : "+v"(w), "+v"(w2));  // computed here, not sunk next to the PV MFMAs
     pb.hi[q] = w;
     pb.lo[q] = w2;
   };
-  // The whole softmax of a step, not overlapped (first step of a pass).
-  auto softmax_all = [&](Probs& t, int st, StepP& out) __attribute__((always_inline)) {
-    max_a(t, st, st >= nplain);
-    max_b(t, st, st >= nplain);
-    step_exponent(t);
-#pragma unroll
-    for (int k = 0; k < 16; ++k) exp_piece(t, k);
-#pragma unroll
-    for (int q = 4; q < 8; ++q) hilo_piece(t.b, q, out.pb);
-    out.pa = t.a;
-    out.ef = t.ef;
-  };
-
   f32x16 o[16];  // O^T blocks: register r of block d = row wrow0 + n, column 32 d + tok_of(gg, r)
 
-  // O^T += V^T . [hi | lo]^T of step st over the 16 blocks of 32 value columns, one V fragment
-  // (64 tokens x 32 columns) per block shared by the hi and lo MFMAs.  With kNext, the whole
-  // softmax of the next step's scores t fills the 32 gaps between these MFMAs, ending in its
-  // P bytes nx.
-  auto pv_step = [&](int st, const StepP& cur, Probs& t, StepP& nx, bool mask_next,
-                     auto with_next) __attribute__((always_inline)) {
-    constexpr bool kNext = decltype(with_next)::value;
-    const uint32_t sb = step_base(st);
-    const int escale = 127 + cur.ef;
-    i32x2 va[16][4];
-#pragma unroll
-    for (int d = 0; d < kVAhead; ++d) {
-      va[d][0] = lds_read_tr8(lds, sb + vrow0 + 32 * d);
-      va[d][1] = lds_read_tr8(lds, sb + vrow1 + 32 * d);
-      va[d][2] = lds_read_tr8(lds, sb + kSlot + vrow0 + 32 * d);
-      va[d][3] = lds_read_tr8(lds, sb + kSlot + vrow1 + 32 * d);
-    }
-    // gap g (after PV MFMA g): 0 max_a, 1 max_b, 2 exponent, 3..18 exp pieces, 20, 22, 24,
-    // 26 hi/lo of tile b
-    auto gap = [&](int g) __attribute__((always_inline)) {
-      if constexpr (kNext) {
-        sched_fence();
-        if (g == 0) max_a(t, st + 1, mask_next);  // 2 MFMAs after the last one that wrote t.a
-        else if (g == 1) max_b(t, st + 1, mask_next);  // 2 MFMAs after the last write of t.b
-        else if (g == 2) step_exponent(t);
-        else if (g <= 18) exp_piece(t, g - 3);
-        else if (g >= 20 && g <= 26 && g % 2 == 0) hilo_piece(t.b, 4 + (g - 20) / 2, nx.pb);
-        sched_fence();
-      }
-    };
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      if (d + kVAhead < 16) {
-        const int e = d + kVAhead;
-        va[e][0] = lds_read_tr8(lds, sb + vrow0 + 32 * e);
-        va[e][1] = lds_read_tr8(lds, sb + vrow1 + 32 * e);
-        va[e][2] = lds_read_tr8(lds, sb + kSlot + vrow0 + 32 * e);
-        va[e][3] = lds_read_tr8(lds, sb + kSlot + vrow1 + 32 * e);
-      }
-      VFrag vf;
-      vf.h[0] = va[d][0];
-      vf.h[1] = va[d][1];
-      vf.h[2] = va[d][2];
-      vf.h[3] = va[d][3];
-      const i32x8 vb = vf.v;
-      if (d == 0) mfma_pv<true>(o[d], vb, cur.pb.hi, escale);
-      else mfma_pv<false>(o[d], vb, cur.pb.hi, escale);
-      gap(2 * d);
-      mfma_pv<false>(o[d], vb, cur.pb.lo, escale);
-      gap(2 * d + 1);
-    }
-    if constexpr (kNext) {
-      nx.ef = t.ef;
-      nx.pa = t.a;
-    }
+  // K fragment of QK MFMA q of a step (tile q & 1, channel block q >> 1).
+  auto read_k = [&](uint32_t sb, int q) __attribute__((always_inline)) -> i32x8 {
+    const uint32_t a = sb + (uint32_t)((q & 1) * kSlot) + krow + 64u * (uint32_t)(q >> 1);
+    return cat8(lds_read16(lds, a), lds_read16(lds, a + 16));
+  };
+  // V fragment of value block d of a step: four transposed 8-byte reads.
+  auto read_v = [&](uint32_t sb, int d, i32x2 (&va)[4]) __attribute__((always_inline)) {
+    va[0] = lds_read_tr8(lds, sb + vrow0 + 32 * d);
+    va[1] = lds_read_tr8(lds, sb + vrow1 + 32 * d);
+    va[2] = lds_read_tr8(lds, sb + kSlot + vrow0 + 32 * d);
+    va[3] = lds_read_tr8(lds, sb + kSlot + vrow1 + 32 * d);
+  };
+  // Softmax of a step in kPieces pieces: 0 max over tile a, 1 max over tile b, 2 step
+  // exponent, 3..18 exp2 of scores 2j, 2j+1 of [a | b], 19..34 their hi/lo bytes.
+  constexpr int kPieces = 35;
+  auto softmax_piece = [&](Probs& t, int st, bool masked, int k, StepP& out)
+      __attribute__((always_inline)) {
+    if (k == 0) max_a(t, st, masked);
+    else if (k == 1) max_b(t, st, masked);
+    else if (k == 2) step_exponent(t);
+    else if (k <= 18) exp_piece(t, k - 3);
+    else if (k - 19 < 8 && (k & 1) != 0)
+      hilo_pair(t.a, 2 * (k - 19), (k - 19) >> 1, std::false_type{}, out.pb);
+    else if (k - 19 < 8)
+      hilo_pair(t.a, 2 * (k - 19), (k - 19) >> 1, std::true_type{}, out.pb);
+    else if ((k & 1) != 0)
+      hilo_pair(t.b, 2 * (k - 27), (k - 19) >> 1, std::false_type{}, out.pb);
+    else
+      hilo_pair(t.b, 2 * (k - 27), (k - 19) >> 1, std::true_type{}, out.pb);
+    if (k == kPieces - 1) out.ef = t.ef;
   };
 
-  // Steady-state step st: QK of step st + 1 (with the DMA of step st + 3 between its MFMAs),
-  // then P.V of step st (with the softmax of step st + 1 between its MFMAs).
+  // One pipeline stage st: the QK MFMAs of step st + 1 (scores into sn, when kQK), the softmax
+  // of step st (scores sc -> P bytes pn) and the P.V MFMAs of step st - 1 (P bytes pp, when
+  // kPV).  The three are independent, so the MFMAs interleave as (QK, PV hi, PV lo) x 16, QK,
+  // QK and every gap between two MFMAs carries an even share of the softmax pieces, the K and
+  // V fragment reads and the DMA of step st + 2.  Ends with every DMA landed and a barrier.
   StepPages sp_next;  // pages of the next step to issue
-  auto iteration = [&](int st, StepP& cur, StepP& nx) __attribute__((always_inline)) {
-    Probs t;
-    const uint32_t sb1 = step_base(st + 1);
-    KPair kp[9];
-#pragma unroll
-    for (int c = 0; c < kKAhead; ++c) kp[c] = read_kpair(sb1, c);
-    // the DMA of step st + 3 goes into the slot that step st - 1 left: resources in gaps 0
-    // and 4, two DMA instructions per gap after that
-    const uint32_t slot3 = slot_of(st + 3);
+  auto stage = [&](int st, Probs& sc, Probs& sn, const StepP& pp, StepP& pn, auto qk_c,
+                   auto pv_c) __attribute__((always_inline)) {
+    constexpr bool kQK = decltype(qk_c)::value, kPV = decltype(pv_c)::value;
+    static_assert(kQK || kPV, "a stage issues MFMAs");
+    constexpr int nmf = (kQK ? 18 : 0) + (kPV ? 32 : 0);
+    const bool masked = st >= nplain;
+    const uint32_t sbk = step_base(st + 1), sbv = step_base(st + 3);  // (st - 1) mod 4
+    const int escale = 127 + pp.ef;
+    const uint32_t slot2 = slot_of(st + 2);
+    i32x8 kf[18];
+    i32x2 va[16][4];
     __amdgpu_buffer_rsrc_t ra, rb;
-    auto dma_gap = [&](int g) __attribute__((always_inline)) {
+    if constexpr (kQK) {
+      kf[0] = read_k(sbk, 0);
+      kf[1] = read_k(sbk, 1);
+    }
+    if constexpr (kPV) read_v(sbv, 0, va[0]);
+    // resources of the two tiles of step st + 2 (its DMA goes into the slot step st - 2 left)
+    ra = tile_rsrc(2 * (st + 2), sp_next.page_a, sp_next.po_a);
+    rb = tile_rsrc(2 * (st + 2) + 1, sp_next.page_b, sp_next.po_b);
+    // work between MFMA number G and the next one
+    auto gap = [&](auto gc) __attribute__((always_inline)) {
+      constexpr int G = decltype(gc)::value;
       using I0 = std::integral_constant<int, 0>;
       using I1 = std::integral_constant<int, 1>;
       using I2 = std::integral_constant<int, 2>;
       using I3 = std::integral_constant<int, 3>;
       using I4 = std::integral_constant<int, 4>;
       sched_fence();
-      if (g == 0) ra = tile_rsrc(2 * (st + 3), sp_next.page_a, sp_next.po_a);
-      if (g == 1) { tile_dma(ra, slot3, I0{}, I0{}); tile_dma(ra, slot3, I0{}, I1{}); }
-      if (g == 2) { tile_dma(ra, slot3, I0{}, I2{}); tile_dma(ra, slot3, I0{}, I3{}); }
-      if (g == 3) tile_dma(ra, slot3, I0{}, I4{});
-      if (g == 4) rb = tile_rsrc(2 * (st + 3) + 1, sp_next.page_b, sp_next.po_b);
-      if (g == 5) { tile_dma(rb, slot3, I1{}, I0{}); tile_dma(rb, slot3, I1{}, I1{}); }
-      if (g == 6) { tile_dma(rb, slot3, I1{}, I2{}); tile_dma(rb, slot3, I1{}, I3{}); }
-      if (g == 7) tile_dma(rb, slot3, I1{}, I4{});
-      if (g >= 9 && g <= 15 && g % 2 == 1) hilo_piece(cur.pa, (g - 9) / 2, cur.pb);  // tile a
+      // the ten DMA instructions (five per tile), spread over the stage's gaps: instruction i
+      // after MFMA 1 + floor(i * (nmf - 1) / 10)
+      constexpr auto dma_gap = [](int i) { return 1 + (i * (nmf - 1)) / 10; };
+      if constexpr (G == dma_gap(0)) tile_dma(ra, slot2, I0{}, I0{});
+      if constexpr (G == dma_gap(1)) tile_dma(ra, slot2, I0{}, I1{});
+      if constexpr (G == dma_gap(2)) tile_dma(ra, slot2, I0{}, I2{});
+      if constexpr (G == dma_gap(3)) tile_dma(ra, slot2, I0{}, I3{});
+      if constexpr (G == dma_gap(4)) tile_dma(ra, slot2, I0{}, I4{});
+      if constexpr (G == dma_gap(5)) tile_dma(rb, slot2, I1{}, I0{});
+      if constexpr (G == dma_gap(6)) tile_dma(rb, slot2, I1{}, I1{});
+      if constexpr (G == dma_gap(7)) tile_dma(rb, slot2, I1{}, I2{});
+      if constexpr (G == dma_gap(8)) tile_dma(rb, slot2, I1{}, I3{});
+      if constexpr (G == dma_gap(9)) tile_dma(rb, slot2, I1{}, I4{});
+      static_assert(1 + (9 * (nmf - 1)) / 10 < nmf, "every DMA instruction has a gap");
+      // softmax pieces k with floor(k * nmf / kPieces) == G
+      static_for<kPieces>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr ((k * nmf) / kPieces == G) softmax_piece(sc, st, masked, k, pn);
+      });
       sched_fence();
     };
-#pragma unroll
-    for (int c = 0; c < 9; ++c) {
-      if (c + kKAhead < 9) kp[c + kKAhead] = read_kpair(sb1, c + kKAhead);
-      if (c == 0) t.a = mfma_qk_first(cat8(kp[0].a0, kp[0].a1), qf[0]);
-      else mfma_qk(t.a, cat8(kp[c].a0, kp[c].a1), qf[c]);
-      dma_gap(2 * c);
-      if (c == 0) t.b = mfma_qk_first(cat8(kp[0].b0, kp[0].b1), qf[0]);
-      else mfma_qk(t.b, cat8(kp[c].b0, kp[c].b1), qf[c]);
-      dma_gap(2 * c + 1);
-    }
-    pv_step(st, cur, t, nx, st + 1 >= nplain, std::true_type{});
-    // pages of step st + 4 (scalar loads, waited for after the barrier where no LDS read is
-    // outstanding); step st + 2 landed for every wave and every wave is past step st
+    static_for<50>([&](auto sc_) __attribute__((always_inline)) {
+      constexpr int slot = decltype(sc_)::value;
+      constexpr int G = slot_gap(slot, kQK, kPV);
+      if constexpr (slot_is_qk(slot)) {
+        if constexpr (kQK) {
+          constexpr int q = slot >= 48 ? slot - 32 : slot / 3;  // 0..17
+          if constexpr (q + 2 < 18) kf[q + 2] = read_k(sbk, q + 2);
+          if constexpr (q == 0) sn.a = mfma_qk_first(kf[q], qf[0]);
+          else if constexpr (q == 1) sn.b = mfma_qk_first(kf[q], qf[0]);
+          else if constexpr ((q & 1) != 0) mfma_qk(sn.b, kf[q], qf[q >> 1]);
+          else mfma_qk(sn.a, kf[q], qf[q >> 1]);
+          gap(std::integral_constant<int, G>{});
+        }
+      } else {
+        if constexpr (kPV) {
+          constexpr int d = slot / 3;
+          constexpr bool hi = slot % 3 == 1;
+          if constexpr (hi && d + 1 < 16) read_v(sbv, d + 1, va[d + 1]);
+          VFrag vf;
+          vf.h[0] = va[d][0];
+          vf.h[1] = va[d][1];
+          vf.h[2] = va[d][2];
+          vf.h[3] = va[d][3];
+          if constexpr (hi && d == 0) mfma_pv<true>(o[d], vf.v, pp.pb.hi, escale);
+          else if constexpr (hi) mfma_pv<false>(o[d], vf.v, pp.pb.hi, escale);
+          else mfma_pv<false>(o[d], vf.v, pp.pb.lo, escale);
+          gap(std::integral_constant<int, G>{});
+        }
+      }
+    });
+    // pages of step st + 3 (scalar loads, waited for after the barrier where no LDS read is
+    // outstanding); every DMA so far has landed and every wave is past this stage's reads
     sp_next = next_pages();
-    wait_vmcnt<kLmin>();
+    wait_vmcnt<0>();
     __syncthreads();
     asm volatile("" ::"s"(sp_next.page_a), "s"(sp_next.page_b));
+  };
+  // P.V of the last step, with nothing else to overlap.
+  auto last_pv = [&](int st, const StepP& pp) __attribute__((always_inline)) {
+    const uint32_t sbv = step_base(st);
+    const int escale = 127 + pp.ef;
+    i32x2 va[16][4];
+    read_v(sbv, 0, va[0]);
+    static_for<16>([&](auto dc) __attribute__((always_inline)) {
+      constexpr int d = decltype(dc)::value;
+      if constexpr (d + 1 < 16) read_v(sbv, d + 1, va[d + 1]);
+      VFrag vf;
+      vf.h[0] = va[d][0];
+      vf.h[1] = va[d][1];
+      vf.h[2] = va[d][2];
+      vf.h[3] = va[d][3];
+      if constexpr (d == 0) mfma_pv<true>(o[d], vf.v, pp.pb.hi, escale);
+      else mfma_pv<false>(o[d], vf.v, pp.pb.hi, escale);
+      mfma_pv<false>(o[d], vf.v, pp.pb.lo, escale);
+    });
   };
 
 #pragma unroll 1
@@ -606,7 +651,7 @@ void decode_kernel(const DecodeParams p) {
     // are live within a pass only.
     const StepPages sp0 = next_pages();
     const StepPages sp1 = next_pages();
-    const StepPages sp2 = next_pages();
+    sp_next = next_pages();  // step 2, issued by stage 0
     {
       const int qrows = min(kRows, M - row0);
       const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -627,53 +672,50 @@ void decode_kernel(const DecodeParams p) {
       for (int c = 0; c < 9; ++c)
         qf[c] = cat8(lds_read16(lds, qrow + 64 * c), lds_read16(lds, qrow + 64 * c + 16));
     }
-    __syncthreads();  // the Q slots are free from here on
-    issue_step(2, sp2);
-    sp_next = next_pages();  // step 3
+    wait_vmcnt<kLmin>();  // step 0 has landed (step 1 may still be in flight)
+    __syncthreads();      // ... for every wave; the Q slots are free from here on
 
-    // ---- step 0: scores and P bytes, not overlapped with anything
-    wait_vmcnt<2 * kLmin>();
-    __syncthreads();
-    StepP X, Y;
+    // ---- step 0's scores, not overlapped with anything
+    Probs X, Y;
+    StepP PA, PB;
     {
-      Probs t;
       const uint32_t sb = step_base(0);
 #pragma unroll
       for (int c = 0; c < 9; ++c) {
         const KPair k = read_kpair(sb, c);
         if (c == 0) {
-          t.a = mfma_qk_first(cat8(k.a0, k.a1), qf[0]);
-          t.b = mfma_qk_first(cat8(k.b0, k.b1), qf[0]);
+          X.a = mfma_qk_first(cat8(k.a0, k.a1), qf[0]);
+          X.b = mfma_qk_first(cat8(k.b0, k.b1), qf[0]);
         } else {
-          mfma_qk(t.a, cat8(k.a0, k.a1), qf[c]);
-          mfma_qk(t.b, cat8(k.b0, k.b1), qf[c]);
+          mfma_qk(X.a, cat8(k.a0, k.a1), qf[c]);
+          mfma_qk(X.b, cat8(k.b0, k.b1), qf[c]);
         }
       }
-      mfma_drain2(t.a, t.b);
-      softmax_all(t, 0, X);
+      mfma_drain2(X.a, X.b);
     }
-    // step 1 visible to every wave before the loop reads it
-    wait_vmcnt<kLmin>();
+    wait_vmcnt<0>();  // step 1 has landed
     __syncthreads();
 
-    // two steps per trip, the P buffers X and Y trading roles
-    int st = 0;
-    for (; st + 2 < nsteps; st += 2) {
-      iteration(st, X, Y);
-      iteration(st + 1, Y, X);
+    // ---- the pipeline.  Invariant at the top of the loop: scores of step st in Y, P bytes
+    // of step st - 1 in PA.
+    // (a single-step chunk computes the scores of an empty step 1 here, unused)
+    stage(0, X, Y, PB, PA, std::true_type{}, std::false_type{});
+    int st = 1;
+    for (; st + 2 <= nsteps - 1; st += 2) {
+      stage(st, Y, X, PA, PB, std::true_type{}, std::true_type{});
+      stage(st + 1, X, Y, PB, PA, std::true_type{}, std::true_type{});
     }
-    if (st + 1 < nsteps) {
-      iteration(st, X, Y);
+    if (st <= nsteps - 2) {
+      stage(st, Y, X, PA, PB, std::true_type{}, std::true_type{});
       ++st;
-      X = Y;
+      Y = X;
+      PA = PB;
     }
-    {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) hilo_piece(X.pa, q, X.pb);
-      Probs unused_t;
-      StepP unused_p;
-      pv_step(st, X, unused_t, unused_p, false, std::false_type{});  // the last step
+    if (nsteps >= 2) {  // softmax of the last step beside the P.V of the one before
+      stage(nsteps - 1, Y, X, PA, PB, std::false_type{}, std::true_type{});
+      PA = PB;
     }
+    last_pv(nsteps - 1, PA);
     mfma_drain_acc(o[15]);
 #pragma unroll
     for (int d = 0; d < 15; ++d) acc_fence(o[d]);

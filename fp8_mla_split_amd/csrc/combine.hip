@@ -5,11 +5,12 @@
 // next (one cache latency per partial) by one that issues every partial's load first and then
 // accumulates from registers.  Here a row's 512 value columns are split over kCw workgroups
 // (kCw * rows workgroups in all, so a batch-1 merge still spreads over the whole chip); a
-// workgroup has NW = ceil(S / (16 kCw)) waves (at most 16) and each wave owns 16 kCw splits
-// per batch.  A lane covers 8 columns (16 bytes) of one split row, so one wave-wide load
-// instruction fetches kCw split rows; a wave issues its whole batch of 16 loads (and the 16
-// log-sum-exps) before it touches any of them, keeps a running max of its splits' lse and
-// rescales as it goes, and the workgroup's lanes meet in LDS at the end.
+// workgroup has NW = ceil(S / (B kCw)) waves (at most 16) and each wave owns B kCw splits per
+// batch, with B = 4, 8 or 16 load instructions per batch as S requires.  A lane covers 8
+// columns (16 bytes) of one split row, so one wave-wide load instruction fetches kCw split
+// rows; a wave issues its whole batch of loads (and the log-sum-exps) before it touches any of
+// them, keeps a running max of its splits' lse and rescales as it goes, and the workgroup's
+// lanes meet in LDS at the end.
 //
 //   M = max_s lse_s;  w_s = exp(lse_s - M);  O = v_scale * sum_s w_s O_s / sum_s w_s;
 //   lse = M + log sum_s w_s
@@ -22,7 +23,6 @@
 namespace mla {
 namespace {
 
-constexpr int kBatch = 16;   // load instructions in flight per wave
 constexpr int kCw = 2;       // workgroups (column chunks) per output row
 constexpr int kLanesPerRow = 64 / kCw;  // lanes covering one split row's chunk
 constexpr int kMaxWaves = 16;
@@ -39,10 +39,12 @@ struct Partial {
   float acc[8];
 };
 
+// kBatch: load instructions a wave issues before it accumulates (kBatch * kCw splits).
+template <int kBatch>
 __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
     const uint16_t* __restrict__ po, const float* __restrict__ pl, int S, int R, float v_scale,
     uint16_t* __restrict__ out, float* __restrict__ out_lse) {
-  __shared__ Partial red[kMaxWaves * 64];
+  extern __shared__ Partial red[];  // one entry per thread
   const int row = blockIdx.x / kCw;  // b * R + r
   const int chunk = blockIdx.x - row * kCw;
   const int b = row / R, r = row - b * R;
@@ -124,13 +126,26 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
 
 }  // namespace
 
-hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
-                          float v_scale, uint16_t* out, float* out_lse, hipStream_t s) {
+template <int kBatch>
+static void launch_batch(const uint16_t* po, const float* pl, int batch, int splits, int rows,
+                         float v_scale, uint16_t* out, float* out_lse, hipStream_t s) {
   const int64_t blocks = (int64_t)batch * rows * kCw;
   int nw = (splits + kBatch * kCw - 1) / (kBatch * kCw);
   nw = nw < 1 ? 1 : (nw > kMaxWaves ? kMaxWaves : nw);
-  combine_kernel<<<(unsigned)blocks, 64 * nw, 0, s>>>(po, pl, splits, rows, v_scale, out,
-                                                       out_lse);
+  const size_t lds = sizeof(Partial) * 64 * nw;
+  combine_kernel<kBatch><<<(unsigned)blocks, 64 * nw, lds, s>>>(po, pl, splits, rows, v_scale,
+                                                                 out, out_lse);
+}
+
+hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
+                          float v_scale, uint16_t* out, float* out_lse, hipStream_t s) {
+  // as many loads in flight per wave as there are splits to cover, up to 16
+  if (splits <= 4 * kCw)
+    launch_batch<4>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
+  else if (splits <= 8 * kCw)
+    launch_batch<8>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
+  else
+    launch_batch<16>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
   return hipGetLastError();
 }
 

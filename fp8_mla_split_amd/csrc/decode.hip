@@ -277,27 +277,52 @@ void decode_kernel(const DecodeParams p) {
   const int G = p.groups, S = p.num_splits, M = p.rows;
   const int id = blockIdx.x;
   const int kx = id >> 3;
-  const int g = kx % G;
-  const int u = (kx / G) * 8 + (id & 7);
+  const int kxg = (int)fast_div((uint32_t)kx, p.div_groups);
+  const int g = kx - kxg * G;
+  const int u = kxg * 8 + (id & 7);
   if (u >= p.batch * S) return;
-  const int b = u / S, s = u - b * S;
+  const int b = (int)fast_div((uint32_t)u, p.div_splits), s = u - b * S;
 
   // Wave-uniform scalars come from the constant address space (scalar loads, lgkmcnt).
   const __attribute__((address_space(4))) int32_t* seq_lens =
       (const __attribute__((address_space(4))) int32_t*)p.seq_lens;
   const __attribute__((address_space(4))) int32_t* page_table =
       (const __attribute__((address_space(4))) int32_t*)p.page_table;
+  const int row0 = g * kRows;
+  const uint32_t wave_lds = lds_base + (uint32_t)wave * 1024u;
+
+  // ---- the workgroup's 128 query rows (contiguous in q8) go to tile slots 4..7 first: they
+  // do not depend on the sequence length, so their DMA overlaps the length and page-table
+  // loads below.  18 DMA instructions per wave; instruction i = wave + 4 j moves bytes
+  // [1024 i, 1024 (i + 1)) of the rows.
+  auto stage_q = [&]() __attribute__((always_inline)) {
+    const int qrows = min(kRows, M - row0);
+    const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.q8 + ((int64_t)b * M + row0) * kD), 0, qrows * kD, 0x00020000);
+    const uint32_t qvoff = (uint32_t)wave * 1024u + 16u * (uint32_t)lane;
+#pragma unroll
+    for (int j = 0; j < kQDma / 4; ++j)
+      dma16_s(wave_lds, qvoff + 4096u * j, qrsrc, kQSlot * kSlot + 4096 * j);
+  };
+  stage_q();
+  // Prefetch the page-table entry of this chunk's first tile as it would be for a request of
+  // the host's maximum length (exact for equal lengths), alongside the length itself.
+  const int64_t pt_row = (int64_t)b * p.max_pages;
+  const int pt_hint = page_table[pt_row + min((int)fast_div((uint32_t)(s * p.tiles_hint),
+                                                            p.div_tpp),
+                                              p.max_pages - 1)];
   int L = seq_lens[b];
   const int Lmax = p.max_pages * p.page_size;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int ntiles_all = (L + kTile - 1) / kTile;
-  const int per = (ntiles_all + S - 1) / S;
+  const int per = (int)fast_div((uint32_t)(ntiles_all + S - 1), p.div_splits);
   const int t_begin = s * per;
   const int ntiles = max(min(t_begin + per, ntiles_all) - t_begin, 0);
 
-  const int row0 = g * kRows;
   const int64_t prow = (int64_t)(b * S + s) * M;  // first partial row of this (b, s)
+  asm volatile("" ::"s"(pt_hint));  // (issued above; consumed so that it stays)
   if (ntiles == 0) {
+    wait_vmcnt<0>();  // the Q DMA lands before the workgroup's LDS is released
     for (int i = threadIdx.x; i < kRows; i += 256)
       if (row0 + i < M) p.partial_lse[prow + row0 + i] = -INFINITY;
     return;
@@ -307,8 +332,8 @@ void decode_kernel(const DecodeParams p) {
   const int R = wrow0 + n;  // this lane's query row (score, P and O layout)
   const bool row_ok = R < M;
   // last visible position of the row (bottom-right causal); rows past M are never stored
-  const int lim = row_ok ? L - p.q_tokens + R / p.heads : 0x7FFFFFFF;
-  const int lim_min = L - p.q_tokens + wrow0 / p.heads;
+  const int lim = row_ok ? L - p.q_tokens + (int)fast_div((uint32_t)R, p.div_heads) : 0x7FFFFFFF;
+  const int lim_min = L - p.q_tokens + (int)fast_div((uint32_t)wrow0, p.div_heads);
   const int nsteps = (ntiles + 1) / 2;
   // Steps 0 .. nplain-1 need no masking: both tiles in the chunk and every position visible
   // to every row of this wave (tile 2j + 1 ends at (t_begin + 2j + 2) * 32 - 1 <= lim_min).
@@ -319,8 +344,8 @@ void decode_kernel(const DecodeParams p) {
   }
   const int P = p.page_size;
   const int tpp = P / kTile;  // tiles per page
-  const int64_t pt_row = (int64_t)b * p.max_pages;
-  const int pe_last = (t_begin + ntiles - 1) / tpp;  // page-table entry of the chunk's last tile
+  // page-table entry of the chunk's last tile
+  const int pe_last = (int)fast_div((uint32_t)(t_begin + ntiles - 1), p.div_tpp);
 
   // ---- DMA lane offsets.  Of a tile's 19 DMA instructions, wave w issues k = w + 4 i
   // (i < 4, and i = 4 for waves 0..2): LDS bytes 1024 w + 4096 i of the slot.  Chunk
@@ -333,11 +358,11 @@ void decode_kernel(const DecodeParams p) {
     const uint32_t row = pch / 37u;
     voff[i] = 16u * (pch - row);
   }
-  const uint32_t wave_lds = lds_base + (uint32_t)wave * 1024u;
 
   // ---- page cursor: page-table entry and tile-within-page of tile 2j of the next step j
   // to prepare, advanced two tiles per step without divisions.
-  int cur_pe = t_begin / tpp;
+  const int pe_first = (int)fast_div((uint32_t)t_begin, p.div_tpp);
+  int cur_pe = pe_first;
   int cur_po = t_begin - cur_pe * tpp;
   struct StepPages {
     int page_a, po_a, page_b, po_b;
@@ -640,30 +665,20 @@ void decode_kernel(const DecodeParams p) {
 
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int d = 0; d < 16; ++d) o[d] = (f32x16){0.f};
     rs.l_run = 0.f;
-    cur_pe = t_begin / tpp;
+    cur_pe = pe_first;
     cur_po = t_begin - cur_pe * tpp;
 
-    // ---- stage the workgroup's 128 query rows (contiguous in q8) in tile slots 4..7 with
-    // steps 0 and 1 in flight beside them.  Each pass stages them again, so the Q fragments
-    // are live within a pass only.
+    // ---- the query rows (staged above for the first pass; again for a second pass, since
+    // the Q fragments are live within a pass only) with steps 0 and 1 in flight beside them
     const StepPages sp0 = next_pages();
     const StepPages sp1 = next_pages();
     sp_next = next_pages();  // step 2, issued by stage 0
-    {
-      const int qrows = min(kRows, M - row0);
-      const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.q8 + ((int64_t)b * M + row0) * kD), 0, qrows * kD, 0x00020000);
-      // instruction i = wave + 4 j moves bytes [1024 i, 1024 (i + 1)) of the rows
-      const uint32_t qvoff = (uint32_t)wave * 1024u + 16u * (uint32_t)lane;
-#pragma unroll
-      for (int j = 0; j < kQDma / 4; ++j)
-        dma16_s(wave_lds, qvoff + 4096u * j, qrsrc, kQSlot * kSlot + 4096 * j);
-    }
+    if (pass > 0) stage_q();
     issue_step(0, sp0);
     issue_step(1, sp1);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) o[d] = (f32x16){0.f};  // while the DMAs are in flight
     wait_vmcnt<2 * kLmin>();  // this wave's Q chunks have landed
     __syncthreads();
     {

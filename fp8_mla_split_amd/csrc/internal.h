@@ -11,6 +11,30 @@ constexpr int kTile = 32;  // KV tokens per tile (one LDS ring slot)
 constexpr int kMaxRows = 65536;
 constexpr int kMaxSplitsCombine = 4096;
 
+// Unsigned division by a divisor fixed at launch (Granlund & Montgomery, "Division by
+// invariant integers using multiplication"): n / d == (t + ((n - t) >> s1)) >> s2 with
+// t = mulhi(n, m), for every 32-bit n.
+struct FastDiv {
+  uint32_t d, m;
+  int s1, s2;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  int l = 0;
+  while (l < 32 && (1ull << l) < d) ++l;  // ceil(log2 d)
+  FastDiv f;
+  f.d = d;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 1 ? l - 1 : 0;
+  return f;
+}
+
+__host__ __device__ inline uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  const uint32_t t = (uint32_t)(((uint64_t)n * f.m) >> 32);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 struct DecodeParams {
   const uint8_t* q8;
   const uint8_t* kv;
@@ -21,6 +45,8 @@ struct DecodeParams {
   int batch, q_tokens, heads, rows;   // rows = q_tokens * heads
   int page_size, max_pages, num_splits, groups;
   int64_t page_bytes;                 // page_size * 576
+  int tiles_hint;                     // 32-token tiles per split for the host's maximum length
+  FastDiv div_splits, div_groups, div_heads, div_tpp;  // by num_splits, groups, heads, page_size/32
   float c2;                           // q_scale * kv_scale * softmax_scale * log2(e)
   float kv_scale;
 };

@@ -159,9 +159,19 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   p.rows = (int)M;
   p.page_size = page_size;
   p.page_bytes = (int64_t)page_size * mla::kD;
+  {  // prefetch hint only (any value is safe): a split's tiles if every length were the maximum
+    const int64_t ms = max_seq_len < 1 ? 1 : max_seq_len;
+    const int64_t tiles = cdiv(ms, (int64_t)mla::kTile);
+    const int64_t per = cdiv(tiles, (int64_t)S);
+    p.tiles_hint = (int)(per > 0x7FFF ? 0x7FFF : per);
+  }
   p.max_pages = max_pages;
   p.num_splits = S;
   p.groups = (int)groups;
+  p.div_splits = mla::make_fastdiv((uint32_t)S);
+  p.div_groups = mla::make_fastdiv((uint32_t)groups);
+  p.div_heads = mla::make_fastdiv((uint32_t)heads);
+  p.div_tpp = mla::make_fastdiv((uint32_t)(page_size / mla::kTile));
   p.c2 = (float)((double)q_scale * kv_scale * softmax_scale * 1.4426950408889634);
   p.kv_scale = kv_scale;
   const hipError_t e = mla::launch_decode(p, r, (hipStream_t)stream);

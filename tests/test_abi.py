@@ -158,3 +158,21 @@ def test_split_count_follows_cu_count_and_context(lib):
     assert s_128 < s_256
     assert s_short < s_256
     assert _plan(lib, 64, 1, 128, 131072, 256)[1] < s_256
+
+
+def test_graft_entry_build_imports_the_binding_in_a_fresh_process():
+    """build() compiles and then imports the binding; the import half runs here in a fresh
+    interpreter (the compile itself is replaced by a no-op so the test stays fast)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "import fp8_mla_split_amd.build as b\n"
+        "b.build = lambda verbose=False: b.LIB\n"
+        "import __graft_entry__ as g\n"
+        "g.build(); g.build()\n"
+        "import fp8_mla_split_amd as m\n"
+        "assert m.status_string(0) == 'MLA_OK'\n" % ROOT
+    )
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr[-2000:]

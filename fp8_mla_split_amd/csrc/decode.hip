@@ -585,9 +585,10 @@ void decode_kernel(const DecodeParams p) {
       using I3 = std::integral_constant<int, 3>;
       using I4 = std::integral_constant<int, 4>;
       sched_fence();
-      // the ten DMA instructions (five per tile), spread over the stage's gaps: instruction i
-      // after MFMA 1 + floor(i * (nmf - 1) / 10)
-      constexpr auto dma_gap = [](int i) { return 1 + (i * (nmf - 1)) / 10; };
+      // the ten DMA instructions (five per tile), one per gap from the stage's first MFMA on:
+      // the slot they fill was released by the previous stage's barrier, and the sooner they
+      // are issued the more of the stage hides their HBM latency before the wait at its end
+      constexpr auto dma_gap = [](int i) { return i; };
       if constexpr (G == dma_gap(0)) tile_dma(ra, slot2, I0{}, I0{});
       if constexpr (G == dma_gap(1)) tile_dma(ra, slot2, I0{}, I1{});
       if constexpr (G == dma_gap(2)) tile_dma(ra, slot2, I0{}, I2{});
@@ -598,7 +599,7 @@ void decode_kernel(const DecodeParams p) {
       if constexpr (G == dma_gap(7)) tile_dma(rb, slot2, I1{}, I2{});
       if constexpr (G == dma_gap(8)) tile_dma(rb, slot2, I1{}, I3{});
       if constexpr (G == dma_gap(9)) tile_dma(rb, slot2, I1{}, I4{});
-      static_assert(1 + (9 * (nmf - 1)) / 10 < nmf, "every DMA instruction has a gap");
+      static_assert(9 < nmf, "every DMA instruction has a gap");
       // softmax pieces k with floor(k * nmf / kPieces) == G
       static_for<kPieces>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;

@@ -9,8 +9,9 @@
 // batch, with B = 4, 8 or 16 load instructions per batch as S requires.  A lane covers 8
 // columns (16 bytes) of one split row, so one wave-wide load instruction fetches kCw split
 // rows; a wave issues its whole batch of loads (and the log-sum-exps) before it touches any of
-// them, keeps a running max of its splits' lse and rescales as it goes, and the workgroup's
-// lanes meet in LDS at the end.
+// them, and keeps a running max of its splits' lse, rescaling as it goes.  At the end the two
+// halves of each wave merge across lanes in registers, and the waves (if more than one) meet
+// in LDS, where wave 0 merges their entries, again half in each lane half.
 //
 //   M = max_s lse_s;  w_s = exp(lse_s - M);  O = v_scale * sum_s w_s O_s / sum_s w_s;
 //   lse = M + log sum_s w_s
@@ -34,21 +35,88 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 struct Partial {
   float m, ws;
   float acc[8];
 };
 
+// (m, ws, acc) of a and b merged into a: both rescaled to the larger m.  A side that saw no
+// live split (m = -inf) contributes nothing; two such sides stay empty.
+__device__ __forceinline__ void merge_into(Partial& a, const Partial& b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return;
+  const float sa = __expf(a.m - M), sb = __expf(b.m - M);  // exp(-inf) = 0
+  a.ws = sa * a.ws + sb * b.ws;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) a.acc[c] = sa * a.acc[c] + sb * b.acc[c];
+  a.m = M;
+}
+
+// The partials of lanes l mod 32 (lo) and l mod 32 + 32 (hi), in every lane: one
+// v_permlane32_swap per value, whose two results are those two lanes' values in either half.
+__device__ __forceinline__ void lane_halves(const Partial& p, Partial& lo, Partial& hi) {
+  const float* src = &p.m;
+  float* dlo = &lo.m;
+  float* dhi = &hi.m;
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(src[i]),
+                                                    __float_as_uint(src[i]), false, false);
+    dlo[i] = __uint_as_float(r[0]);
+    dhi[i] = __uint_as_float(r[1]);
+  }
+}
+
+// Both halves of the wave end up holding the merge of lanes l mod 32 and l mod 32 + 32.
+__device__ __forceinline__ void merge_halves(Partial& p) {
+  Partial hi;
+  lane_halves(p, p, hi);
+  merge_into(p, hi);
+}
+
+// Column group pos of the nw per-wave entries in LDS, merged: lane half h takes entries
+// h, h + 2, h + 4, ... (merge_halves then joins the two halves).  Every read is unconditional
+// (an index past nw reads entry nw - 1, which is then ignored), so all of them are in flight
+// together.
+__device__ __forceinline__ Partial merge_entries(const Partial* red, int nw, int pos, int h) {
+  Partial e[kMaxWaves / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxWaves / 2; ++k) e[k] = red[min(2 * k + h, nw - 1) * kLanesPerRow + pos];
+  Partial q;
+  q.m = -INFINITY;
+  q.ws = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) q.acc[c] = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxWaves / 2; ++k)
+    if (2 * k + h < nw) q.m = fmaxf(q.m, e[k].m);
+  if (q.m == -INFINITY) return q;
+#pragma unroll
+  for (int k = 0; k < kMaxWaves / 2; ++k) {
+    // 0 for an entry past nw or one that saw no live split
+    const float sc = 2 * k + h < nw ? __expf(e[k].m - q.m) : 0.f;
+    q.ws = fmaf(sc, e[k].ws, q.ws);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) q.acc[c] = fmaf(sc, e[k].acc[c], q.acc[c]);
+  }
+  return q;
+}
+
 // kBatch: load instructions a wave issues before it accumulates (kBatch * kCw splits).
 template <int kBatch>
 __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
-    const uint16_t* __restrict__ po, const float* __restrict__ pl, int S, int R, float v_scale,
-    uint16_t* __restrict__ out, float* __restrict__ out_lse) {
-  extern __shared__ Partial red[];  // one entry per thread
+    const uint16_t* __restrict__ po, const float* __restrict__ pl, int S, int R, int nw,
+    float v_scale, uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+  static_assert(kCw == 2, "the two split rows of a load sit in lanes l and l + 32");
+  // all arguments in one batch of scalar loads (one trip to the argument memory)
+  asm volatile("" ::"s"(po), "s"(pl), "s"(S), "s"(R), "s"(nw), "s"(v_scale), "s"(out),
+               "s"(out_lse));
+  extern __shared__ Partial red[];  // one entry per (wave, column group)
   const int row = blockIdx.x / kCw;  // b * R + r
   const int chunk = blockIdx.x - row * kCw;
   const int b = row / R, r = row - b * R;
-  const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane / kLanesPerRow;             // which of the kCw split rows of a load
   const int pos = lane - sub * kLanesPerRow;       // 16-byte column group within the chunk
@@ -66,15 +134,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
 
   // split of load j of batch t: ((t * nw + wave) * kBatch + j) * kCw + sub
   for (int s0 = wave * kBatch * kCw; s0 < S; s0 += nw * kBatch * kCw) {
-    uint4 v[kBatch];
+    u32x4 v[kBatch];
     float l[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {  // every load of the batch first
       const int s = s0 + j * kCw + sub;
       const int sc = min(s, S - 1);
-      l[j] = s < S ? lse[(int64_t)sc * R] : -INFINITY;
-      v[j] = *(const uint4*)(o + (int64_t)sc * ostride);
+      l[j] = lse[(int64_t)sc * R];  // loaded unconditionally (no branch per load)
+      v[j] = *(const u32x4*)(o + (int64_t)sc * ostride);
     }
+    // every load of the batch is in flight before the first is used (the compiler would
+    // otherwise sink them into the accumulation below, one round trip each)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) asm volatile("" ::"v"(l[j]), "v"(v[j]));
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j * kCw + sub >= S) l[j] = -INFINITY;
     float bm = p.m;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) bm = fmaxf(bm, l[j]);
@@ -95,24 +171,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
       p.m = bm;
     }
   }
-  red[threadIdx.x] = p;
-  __syncthreads();
-  if (wave != 0 || sub != 0) return;
-
-  // lane pos of wave 0 merges the nw * kCw partials of its column group
-  float M = -INFINITY;
-  for (int k = 0; k < nw * kCw; ++k)
-    M = fmaxf(M, red[(k / kCw) * 64 + (k % kCw) * kLanesPerRow + pos].m);
-  float ws = 0.f, tot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    for (int k = 0; k < nw * kCw; ++k) {
-      const Partial& q = red[(k / kCw) * 64 + (k % kCw) * kLanesPerRow + pos];
-      const float sc = __expf(q.m - M);  // 0 for a partial that saw no live split
-      ws += sc * q.ws;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) tot[c] = fmaf(sc, q.acc[c], tot[c]);
-    }
+  // lanes l and l + 32 hold the same columns of different splits: merge them in registers;
+  // with several waves, these meet in LDS and wave 0 merges their entries
+  merge_halves(p);
+  if (nw > 1) {
+    if (lane < kLanesPerRow) red[wave * kLanesPerRow + pos] = p;
+    __syncthreads();
+    if (wave != 0) return;
+    p = merge_entries(red, nw, pos, lane >> 5);
+    merge_halves(p);
   }
+  if (lane >= kLanesPerRow) return;
+  const float ws = p.ws, M = p.m;
+  const float* tot = p.acc;
   const float f = ws > 0.f ? v_scale / ws : 0.f;
   uint4 packed;
   packed.x = (uint32_t)bf16_rne(tot[0] * f) | ((uint32_t)bf16_rne(tot[1] * f) << 16);
@@ -132,9 +203,9 @@ static void launch_batch(const uint16_t* po, const float* pl, int batch, int spl
   const int64_t blocks = (int64_t)batch * rows * kCw;
   int nw = (splits + kBatch * kCw - 1) / (kBatch * kCw);
   nw = nw < 1 ? 1 : (nw > kMaxWaves ? kMaxWaves : nw);
-  const size_t lds = sizeof(Partial) * 64 * nw;
-  combine_kernel<kBatch><<<(unsigned)blocks, 64 * nw, lds, s>>>(po, pl, splits, rows, v_scale,
-                                                                 out, out_lse);
+  const size_t lds = sizeof(Partial) * kLanesPerRow * nw;
+  combine_kernel<kBatch><<<(unsigned)blocks, 64 * nw, lds, s>>>(po, pl, splits, rows, nw,
+                                                                 v_scale, out, out_lse);
 }
 
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,

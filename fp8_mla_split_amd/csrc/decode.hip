@@ -268,6 +268,15 @@ void decode_kernel(const DecodeParams p) {
   const uint32_t lds_base =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
+  // Every argument the set-up reads goes out in one batch of scalar loads and is waited for
+  // once (left alone, the compiler issues them in three dependent rounds around the early
+  // exit below, each a trip to the argument memory).
+  asm volatile("" ::"s"(p.q8), "s"(p.page_table), "s"(p.seq_lens), "s"(p.batch),
+               "s"(p.q_tokens), "s"(p.rows), "s"(p.page_size), "s"(p.max_pages),
+               "s"(p.num_splits), "s"(p.groups), "s"(p.tiles_hint), "s"(p.div_splits.m),
+               "s"(p.div_splits.s1), "s"(p.div_splits.s2), "s"(p.div_groups.m),
+               "s"(p.div_groups.s1), "s"(p.div_groups.s2), "s"(p.div_tpp.m), "s"(p.div_tpp.s1),
+               "s"(p.div_tpp.s2));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 31, gg = lane >> 5;

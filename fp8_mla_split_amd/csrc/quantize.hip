@@ -40,11 +40,15 @@ __device__ __forceinline__ uint8_t encode1(float t) {
   return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(t), 0.0f, 0, false) & 0xFF);
 }
 
-__global__ __launch_bounds__(256) void quantize_vec16(const float4* __restrict__ src,
-                                                      uint4* __restrict__ dst, int64_t n16,
-                                                      float scale) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+// Workgroups of kThreads threads; stride = grid * kThreads comes in as an argument, so the
+// kernel reads nothing but its arguments (all fetched in one batch) before its first load.
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void quantize_vec16(const float4* __restrict__ src,
+                                                           uint4* __restrict__ dst, int64_t n16,
+                                                           int64_t stride, float scale) {
+  asm volatile("" ::"s"(src), "s"(dst), "s"(n16), "s"(stride), "s"(scale));
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += stride) {
     const float4 a = src[4 * i + 0], b = src[4 * i + 1], c = src[4 * i + 2], d = src[4 * i + 3];
     uint4 o;
     o.x = encode4(__fdiv_rn(a.x, scale), __fdiv_rn(a.y, scale), __fdiv_rn(a.z, scale),
@@ -60,11 +64,12 @@ __global__ __launch_bounds__(256) void quantize_vec16(const float4* __restrict__
 }
 
 // Element-wise variant for unaligned buffers and for the tail after the 16-element blocks.
-__global__ __launch_bounds__(256) void quantize_scalar(const float* __restrict__ src,
-                                                       uint8_t* __restrict__ dst, int64_t begin,
-                                                       int64_t n, float scale) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+__global__ __launch_bounds__(kThreads) void quantize_scalar(const float* __restrict__ src,
+                                                            uint8_t* __restrict__ dst,
+                                                            int64_t begin, int64_t n,
+                                                            int64_t stride, float scale) {
+  asm volatile("" ::"s"(src), "s"(dst), "s"(begin), "s"(n), "s"(stride), "s"(scale));
+  for (int64_t i = begin + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
     dst[i] = encode1(__fdiv_rn(src[i], scale));
 }
 
@@ -76,16 +81,18 @@ hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scal
   int64_t done = 0;
   if (aligned && n >= 16) {
     const int64_t n16 = n / 16;
-    const int64_t want = (n16 + 255) / 256;
+    const int64_t want = (n16 + kThreads - 1) / kThreads;
     const int grid = (int)(want < 8192 ? want : 8192);
-    quantize_vec16<<<grid, 256, 0, s>>>((const float4*)src, (uint4*)dst, n16, scale);
+    quantize_vec16<<<grid, kThreads, 0, s>>>((const float4*)src, (uint4*)dst, n16,
+                                             (int64_t)grid * kThreads, scale);
     done = n16 * 16;
   }
   if (done < n) {
     const int64_t rest = n - done;
-    const int64_t want = (rest + 255) / 256;
+    const int64_t want = (rest + kThreads - 1) / kThreads;
     const int grid = (int)(want < 8192 ? want : 8192);
-    quantize_scalar<<<grid, 256, 0, s>>>(src, dst, done, n, scale);
+    quantize_scalar<<<grid, kThreads, 0, s>>>(src, dst, done, n, (int64_t)grid * kThreads,
+                                              scale);
   }
   return hipGetLastError();
 }

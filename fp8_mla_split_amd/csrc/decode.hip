@@ -164,6 +164,14 @@ __device__ __forceinline__ void mfma_drain_acc(f32x16& acc) {
 // Orders later reads of acc after the preceding asm (no wait states of its own).
 __device__ __forceinline__ void acc_fence(f32x16& acc) { asm volatile("" : "+a"(acc)); }
 
+// max(a, b, c) in one v_max3_f32 (written out so no canonicalising v_max of each input is
+// added; the inputs are MFMA results or -inf, never signalling NaNs).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // (value of lane n, value of lane n + 32) in every lane n and n + 32, by one
 // v_permlane32_swap (no LDS traffic).
 __device__ __forceinline__ f32x2 row_pair(float x) {
@@ -248,8 +256,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Position of MFMA slot s of a pipeline stage among the MFMAs the stage issues: slots run
-// (QK, PV hi, PV lo) x 16, QK, QK; a stage without QK or without PV skips those slots.
-__host__ __device__ constexpr bool slot_is_qk(int s) { return s >= 48 || s % 3 == 0; }
+// (PV hi, PV lo, QK) x 16, QK, QK; a stage without QK or without PV skips those slots.  A
+// stage opens with P.V, whose first V fragment was read before the previous stage's barrier,
+// so the MFMA pipe restarts at once while the first K fragments are still on their way.
+__host__ __device__ constexpr bool slot_is_qk(int s) { return s >= 48 || s % 3 == 2; }
 __host__ __device__ constexpr int slot_gap(int s, bool qk, bool pv) {
   int g = -1;
   for (int t = 0; t <= s; ++t)
@@ -262,6 +272,7 @@ struct KPair {
   i32x4 a0, a1, b0, b1;
 };
 
+template <bool kPairPages>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
@@ -316,15 +327,15 @@ void decode_kernel(const DecodeParams p) {
   stage_q();
   // Prefetch the page-table entry of this chunk's first tile as it would be for a request of
   // the host's maximum length (exact for equal lengths), alongside the length itself.
-  const int64_t pt_row = (int64_t)b * p.max_pages;
-  const int pt_hint = page_table[pt_row + min((int)fast_div((uint32_t)(s * p.tiles_hint),
-                                                            p.div_tpp),
-                                              p.max_pages - 1)];
+  const __attribute__((address_space(4))) int32_t* ptrow = page_table + (int64_t)b * p.max_pages;
+  const int pt_hint = ptrow[(uint32_t)min((int)fast_div((uint32_t)(s * p.tiles_hint), p.div_tpp),
+                                          p.max_pages - 1)];
   int L = seq_lens[b];
   const int Lmax = p.max_pages * p.page_size;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int ntiles_all = (L + kTile - 1) / kTile;
-  const int per = (int)fast_div((uint32_t)(ntiles_all + S - 1), p.div_splits);
+  // tiles per split, rounded up to whole 64-token steps (so every chunk starts on an even tile)
+  const int per = 2 * (int)fast_div((uint32_t)((ntiles_all + 1) / 2 + S - 1), p.div_splits);
   const int t_begin = s * per;
   const int ntiles = max(min(t_begin + per, ntiles_all) - t_begin, 0);
 
@@ -349,7 +360,7 @@ void decode_kernel(const DecodeParams p) {
   int nplain;
   {
     const int jv = ((lim_min + 1) >> 5) - t_begin - 2;  // 2j <= jv
-    nplain = min(jv < 0 ? 0 : jv / 2 + 1, ntiles / 2);
+    nplain = __builtin_amdgcn_readfirstlane(min(jv < 0 ? 0 : jv / 2 + 1, ntiles / 2));
   }
   const int P = p.page_size;
   const int tpp = P / kTile;  // tiles per page
@@ -369,7 +380,9 @@ void decode_kernel(const DecodeParams p) {
   }
 
   // ---- page cursor: page-table entry and tile-within-page of tile 2j of the next step j
-  // to prepare, advanced two tiles per step without divisions.
+  // to prepare, advanced two tiles per step without divisions.  With an even number of tiles
+  // per page (kPairPages) both tiles of a step lie in one page, since chunks start on even
+  // tiles: one page-table load per step, and tile b's address is tile a's plus one tile.
   const int pe_first = (int)fast_div((uint32_t)t_begin, p.div_tpp);
   int cur_pe = pe_first;
   int cur_po = t_begin - cur_pe * tpp;
@@ -378,30 +391,60 @@ void decode_kernel(const DecodeParams p) {
   };
   auto next_pages = [&]() __attribute__((always_inline)) -> StepPages {
     StepPages sp;
-    int pe_b = cur_pe, po_b = cur_po + 1;
-    if (po_b >= tpp) { po_b = 0; ++pe_b; }
     sp.po_a = cur_po;
-    sp.po_b = po_b;
-    sp.page_a = page_table[pt_row + min(cur_pe, pe_last)];
-    sp.page_b = page_table[pt_row + min(pe_b, pe_last)];
-    cur_po += 2;
-    if (cur_po >= tpp) { cur_po -= tpp; ++cur_pe; }
-    if (cur_po >= tpp) { cur_po -= tpp; ++cur_pe; }
+    sp.page_a = ptrow[(uint32_t)min(cur_pe, pe_last)];
+    if constexpr (kPairPages) {
+      sp.page_b = sp.page_a;
+      sp.po_b = cur_po + 1;
+      cur_po += 2;
+      if (cur_po == tpp) {
+        cur_po = 0;
+        ++cur_pe;
+      }
+    } else {
+      int pe_b = cur_pe, po_b = cur_po + 1;
+      if (po_b >= tpp) { po_b = 0; ++pe_b; }
+      sp.po_b = po_b;
+      sp.page_b = ptrow[(uint32_t)min(pe_b, pe_last)];
+      cur_po += 2;
+      if (cur_po >= tpp) { cur_po -= tpp; ++cur_pe; }
+      if (cur_po >= tpp) { cur_po -= tpp; ++cur_pe; }
+    }
     return sp;
   };
   // rows of the chunk's tiles that lie before the chunk's end (and the sequence's) are loaded;
   // the rest of a slot, and every tile past the chunk, reads as zeros
   const int chunk_end = min(L, (t_begin + ntiles) * kTile);
-  auto tile_rsrc = [&](int ti, int page, int po) __attribute__((always_inline))
-      -> __amdgpu_buffer_rsrc_t {
-    const int T0 = (t_begin + ti) * kTile;
-    int rows = chunk_end - T0;
-    rows = rows < 0 ? 0 : rows;
-    rows = rows > kTile ? kTile : rows;
-    const int nrec = __builtin_amdgcn_readfirstlane(rows * kD);  // scalar, for the resource
-    const uint8_t* base = p.kv + (uint64_t)(uint32_t)page * (uint64_t)p.page_bytes +
-                          (uint32_t)po * (uint32_t)(kTile * kD);
+  const int chunk_rows = chunk_end - t_begin * kTile;  // rows of the chunk from its first tile
+  // bytes of tile ti (of the chunk) that are loaded: clamp(rows left, 0, 32) * 576, in SALU
+  auto tile_bytes = [&](int ti) __attribute__((always_inline)) -> int {
+    int r;
+    asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2\n\ts_mul_i32 %0, %0, %3"
+        : "=&s"(r)
+        : "s"(chunk_rows - ti * kTile), "n"(kTile), "n"(kD)
+        : "scc");
+    return r;
+  };
+  auto make_rsrc = [&](const uint8_t* base, int nrec) __attribute__((always_inline)) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, 0x00020000);
+  };
+  auto tile_base = [&](int page, int po) __attribute__((always_inline)) -> const uint8_t* {
+    if constexpr (kPairPages)  // page_bytes < 2^32: a 32 x 32 -> 64-bit product
+      return p.kv + (uint64_t)(uint32_t)page * (uint32_t)p.page_bytes +
+             (uint32_t)po * (uint32_t)(kTile * kD);
+    else
+      return p.kv + (uint64_t)(uint32_t)page * (uint64_t)p.page_bytes +
+             (uint32_t)po * (uint32_t)(kTile * kD);
+  };
+  // buffer resources of the two tiles of step st
+  auto step_rsrc = [&](int st, const StepPages& sp, __amdgpu_buffer_rsrc_t& ra,
+                       __amdgpu_buffer_rsrc_t& rb) __attribute__((always_inline)) {
+    const uint8_t* base_a = tile_base(sp.page_a, sp.po_a);
+    ra = make_rsrc(base_a, tile_bytes(2 * st));
+    if constexpr (kPairPages)
+      rb = make_rsrc(base_a + kTile * kD, tile_bytes(2 * st + 1));
+    else
+      rb = make_rsrc(tile_base(sp.page_b, sp.po_b), tile_bytes(2 * st + 1));
   };
   // DMA instructions i of tile slot j of a step slot (i = 4 only on waves 0..2)
   auto tile_dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t slot_lds, auto jc, auto ic)
@@ -409,9 +452,8 @@ void decode_kernel(const DecodeParams p) {
     constexpr int j = decltype(jc)::value, i = decltype(ic)::value;
     if (i < 4 || wave < 3) dma16<j * kSlot + i * 4096>(slot_lds, voff[i], rsrc);
   };
-  auto issue_tile = [&](int ti, int page, int po, uint32_t slot_lds, auto jc)
+  auto issue_tile = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t slot_lds, auto jc)
       __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rsrc = tile_rsrc(ti, page, po);
     tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 0>{});
     tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 1>{});
     tile_dma(rsrc, slot_lds, jc, std::integral_constant<int, 2>{});
@@ -425,8 +467,10 @@ void decode_kernel(const DecodeParams p) {
     return wave_lds + (uint32_t)((st % kStepSlots) * 2 * kSlot);
   };
   auto issue_step = [&](int st, const StepPages& sp) __attribute__((always_inline)) {
-    issue_tile(2 * st, sp.page_a, sp.po_a, slot_of(st), std::integral_constant<int, 0>{});
-    issue_tile(2 * st + 1, sp.page_b, sp.po_b, slot_of(st), std::integral_constant<int, 1>{});
+    __amdgpu_buffer_rsrc_t ra, rb;
+    step_rsrc(st, sp, ra, rb);
+    issue_tile(ra, slot_of(st), std::integral_constant<int, 0>{});
+    issue_tile(rb, slot_of(st), std::integral_constant<int, 1>{});
   };
 
   const int G16 = lane >> 4, i16 = lane & 15;
@@ -466,21 +510,29 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = r > c ? -INFINITY : x[r];
   };
+  // max of 16 scores as a tree of depth 3 (five, then two, then one v_max3_f32): a wave
+  // issues in order, so a long dependent chain here would hold back the next MFMA
+  auto max16 = [&](const f32x16& x, float extra) __attribute__((always_inline)) -> float {
+    const float a0 = max3f(x[0], x[1], x[2]), a1 = max3f(x[3], x[4], x[5]);
+    const float a2 = max3f(x[6], x[7], x[8]), a3 = max3f(x[9], x[10], x[11]);
+    const float a4 = max3f(x[12], x[13], x[14]);
+    const float b0 = max3f(a0, a1, a2), b1 = max3f(a3, a4, x[15]);
+    return max3f(b0, b1, extra);
+  };
   auto max_a = [&](Probs& t, int st, bool masked) __attribute__((always_inline)) {
     if (masked) mask_tile(t.a, 2 * st);
-    float m = fmaxf(fmaxf(t.a[0], t.a[1]), t.a[2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, t.a[r]), t.a[r + 1]);
-    t.mpart = fmaxf(m, t.a[15]);
+    t.mpart = max16(t.a, -INFINITY);
     asm volatile("" : "+v"(t.mpart));
   };
   auto max_b = [&](Probs& t, int st, bool masked) __attribute__((always_inline)) {
     if (masked) mask_tile(t.b, 2 * st + 1);
-    float m = fmaxf(fmaxf(t.mpart, t.b[0]), t.b[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) m = fmaxf(fmaxf(m, t.b[r]), t.b[r + 1]);
-    const f32x2 both = row_pair(m);
-    t.mpart = fmaxf(both[0], both[1]) * c2;  // the row's max; c2 > 0
+    t.mpart = max16(t.b, t.mpart);
+    asm volatile("" : "+v"(t.mpart));
+  };
+  // the two halves of the row meet across lanes; the row's max in exp2 units
+  auto max_row = [&](Probs& t) __attribute__((always_inline)) {
+    const f32x2 both = row_pair(t.mpart);
+    t.mpart = max3f(both[0], both[1], -INFINITY) * c2;  // c2 > 0
     asm volatile("" : "+v"(t.mpart));
   };
   auto step_exponent = [&](Probs& t) __attribute__((always_inline)) {
@@ -539,38 +591,44 @@ void decode_kernel(const DecodeParams p) {
     va[2] = lds_read_tr8(lds, sb + kSlot + vrow0 + 32 * d);
     va[3] = lds_read_tr8(lds, sb + kSlot + vrow1 + 32 * d);
   };
-  // Softmax of a step in kPieces pieces: 0 max over tile a, 1 max over tile b, 2 step
-  // exponent, 3..18 exp2 of scores 2j, 2j+1 of [a | b], 19..34 their hi/lo bytes.
-  constexpr int kPieces = 35;
+  // Softmax of a step in kPieces pieces: 0 max over tile a, 1 max over tile b, 2 the row's
+  // max across the lane halves, 3 step exponent, 4..19 exp2 of scores 2j, 2j+1 of [a | b],
+  // 20..35 their hi/lo bytes.
+  constexpr int kPieces = 36;
   auto softmax_piece = [&](Probs& t, int st, bool masked, int k, StepP& out)
       __attribute__((always_inline)) {
     if (k == 0) max_a(t, st, masked);
     else if (k == 1) max_b(t, st, masked);
-    else if (k == 2) step_exponent(t);
-    else if (k <= 18) exp_piece(t, k - 3);
-    else if (k - 19 < 8 && (k & 1) != 0)
-      hilo_pair(t.a, 2 * (k - 19), (k - 19) >> 1, std::false_type{}, out.pb);
-    else if (k - 19 < 8)
-      hilo_pair(t.a, 2 * (k - 19), (k - 19) >> 1, std::true_type{}, out.pb);
-    else if ((k & 1) != 0)
-      hilo_pair(t.b, 2 * (k - 27), (k - 19) >> 1, std::false_type{}, out.pb);
+    else if (k == 2) max_row(t);
+    else if (k == 3) step_exponent(t);
+    else if (k <= 19) exp_piece(t, k - 4);
+    else if (k - 20 < 8 && (k & 1) == 0)
+      hilo_pair(t.a, 2 * (k - 20), (k - 20) >> 1, std::false_type{}, out.pb);
+    else if (k - 20 < 8)
+      hilo_pair(t.a, 2 * (k - 20), (k - 20) >> 1, std::true_type{}, out.pb);
+    else if ((k & 1) == 0)
+      hilo_pair(t.b, 2 * (k - 28), (k - 20) >> 1, std::false_type{}, out.pb);
     else
-      hilo_pair(t.b, 2 * (k - 27), (k - 19) >> 1, std::true_type{}, out.pb);
+      hilo_pair(t.b, 2 * (k - 28), (k - 20) >> 1, std::true_type{}, out.pb);
     if (k == kPieces - 1) out.ef = t.ef;
   };
 
   // One pipeline stage st: the QK MFMAs of step st + 1 (scores into sn, when kQK), the softmax
   // of step st (scores sc -> P bytes pn) and the P.V MFMAs of step st - 1 (P bytes pp, when
-  // kPV).  The three are independent, so the MFMAs interleave as (QK, PV hi, PV lo) x 16, QK,
+  // kPV).  The three are independent, so the MFMAs interleave as (PV hi, PV lo, QK) x 16, QK,
   // QK and every gap between two MFMAs carries an even share of the softmax pieces, the K and
-  // V fragment reads and the DMA of step st + 2.  Ends with every DMA landed and a barrier.
+  // V fragment reads and the DMA of step st + 2.  Ends with the first V fragment of step st
+  // read for the next stage, every DMA landed and a barrier.
   StepPages sp_next;  // pages of the next step to issue
+  i32x2 vnext[4];     // V fragment of block 0 of the step the next stage multiplies
+  // mask_c: whether step st may need masking (false only where the caller knows st < nplain,
+  // so the plain steps carry no masking branch at all).
   auto stage = [&](int st, Probs& sc, Probs& sn, const StepP& pp, StepP& pn, auto qk_c,
-                   auto pv_c) __attribute__((always_inline)) {
+                   auto pv_c, auto mask_c) __attribute__((always_inline)) {
     constexpr bool kQK = decltype(qk_c)::value, kPV = decltype(pv_c)::value;
     static_assert(kQK || kPV, "a stage issues MFMAs");
     constexpr int nmf = (kQK ? 18 : 0) + (kPV ? 32 : 0);
-    const bool masked = st >= nplain;
+    const bool masked = decltype(mask_c)::value && st >= nplain;
     const uint32_t sbk = step_base(st + 1), sbv = step_base(st + 3);  // (st - 1) mod 4
     const int escale = 127 + pp.ef;
     const uint32_t slot2 = slot_of(st + 2);
@@ -581,10 +639,14 @@ void decode_kernel(const DecodeParams p) {
       kf[0] = read_k(sbk, 0);
       kf[1] = read_k(sbk, 1);
     }
-    if constexpr (kPV) read_v(sbv, 0, va[0]);
+    if constexpr (kPV) {
+      va[0][0] = vnext[0];
+      va[0][1] = vnext[1];
+      va[0][2] = vnext[2];
+      va[0][3] = vnext[3];
+    }
     // resources of the two tiles of step st + 2 (its DMA goes into the slot step st - 2 left)
-    ra = tile_rsrc(2 * (st + 2), sp_next.page_a, sp_next.po_a);
-    rb = tile_rsrc(2 * (st + 2) + 1, sp_next.page_b, sp_next.po_b);
+    step_rsrc(st + 2, sp_next, ra, rb);
     // work between MFMA number G and the next one
     auto gap = [&](auto gc) __attribute__((always_inline)) {
       constexpr int G = decltype(gc)::value;
@@ -632,7 +694,7 @@ void decode_kernel(const DecodeParams p) {
       } else {
         if constexpr (kPV) {
           constexpr int d = slot / 3;
-          constexpr bool hi = slot % 3 == 1;
+          constexpr bool hi = slot % 3 == 0;
           if constexpr (hi && d + 1 < 16) read_v(sbv, d + 1, va[d + 1]);
           VFrag vf;
           vf.h[0] = va[d][0];
@@ -646,11 +708,16 @@ void decode_kernel(const DecodeParams p) {
         }
       }
     });
-    // pages of step st + 3 (scalar loads, waited for after the barrier where no LDS read is
-    // outstanding); every DMA so far has landed and every wave is past this stage's reads
+    // V block 0 of step st for the next stage (its slot is not a DMA target until then); pages
+    // of step st + 3 (scalar loads, waited for after the barrier); every DMA so far has landed
+    // and every wave is past this stage's reads
+    read_v(step_base(st), 0, vnext);
     sp_next = next_pages();
     wait_vmcnt<0>();
-    __syncthreads();
+    // A bare s_barrier: this wave's DMA writes have landed (vmcnt above) and every LDS read of
+    // the slot the next DMA overwrites was consumed by this stage's MFMAs, so no LDS or scalar
+    // load needs to drain first (a __syncthreads() fence would wait for them all here).
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::"s"(sp_next.page_a), "s"(sp_next.page_b));
   };
   // P.V of the last step, with nothing else to overlap.
@@ -724,20 +791,22 @@ void decode_kernel(const DecodeParams p) {
     // ---- the pipeline.  Invariant at the top of the loop: scores of step st in Y, P bytes
     // of step st - 1 in PA.
     // (a single-step chunk computes the scores of an empty step 1 here, unused)
-    stage(0, X, Y, PB, PA, std::true_type{}, std::false_type{});
+    using T = std::true_type;
+    using F = std::false_type;
+    stage(0, X, Y, PB, PA, T{}, F{}, T{});
     int st = 1;
     for (; st + 2 <= nsteps - 1; st += 2) {
-      stage(st, Y, X, PA, PB, std::true_type{}, std::true_type{});
-      stage(st + 1, X, Y, PB, PA, std::true_type{}, std::true_type{});
+      stage(st, Y, X, PA, PB, T{}, T{}, T{});
+      stage(st + 1, X, Y, PB, PA, T{}, T{}, T{});
     }
     if (st <= nsteps - 2) {
-      stage(st, Y, X, PA, PB, std::true_type{}, std::true_type{});
+      stage(st, Y, X, PA, PB, T{}, T{}, T{});
       ++st;
       Y = X;
       PA = PB;
     }
     if (nsteps >= 2) {  // softmax of the last step beside the P.V of the one before
-      stage(nsteps - 1, Y, X, PA, PB, std::false_type{}, std::true_type{});
+      stage(nsteps - 1, Y, X, PA, PB, F{}, T{}, T{});
       PA = PB;
     }
     last_pv(nsteps - 1, PA);
@@ -789,7 +858,11 @@ hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t 
   if (rows_per_group != kRows) return hipErrorInvalidValue;
   const int64_t units = (int64_t)p.batch * p.num_splits;
   const int64_t blocks = ((units + 7) / 8) * 8 * p.groups;
-  decode_kernel<<<(unsigned)blocks, 256, 0, s>>>(p);
+  // an even number of tiles per page (and pages under 4 GiB) takes the paired-tile cursor
+  if ((p.page_size / kTile) % 2 == 0 && p.page_bytes < (int64_t(1) << 32))
+    decode_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(p);
+  else
+    decode_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ constexpr double kCombineUs = 3.0;          // the combine launch itself
 double plan_cost(int64_t B, int64_t M, int64_t L, int cu, int64_t S) {
   const int64_t G = cdiv(M, 128);
   const int64_t tiles = cdiv(L, 32);
-  const int64_t steps = cdiv(cdiv(tiles, S), 2);
+  const int64_t steps = cdiv(cdiv(tiles, 2), S);  // chunks are whole 64-token steps
   const int64_t rounds = cdiv(B * S * G, cu);
   const double t_dec = (double)rounds * (kWgOverheadUs + (double)steps * kStepUs);
   const double t_part = (double)(B * S * M) * (1024.0 + 4.0) * 2.0 / kPartialBytesPerUs;
@@ -162,7 +162,7 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   {  // prefetch hint only (any value is safe): a split's tiles if every length were the maximum
     const int64_t ms = max_seq_len < 1 ? 1 : max_seq_len;
     const int64_t tiles = cdiv(ms, (int64_t)mla::kTile);
-    const int64_t per = cdiv(tiles, (int64_t)S);
+    const int64_t per = 2 * cdiv(cdiv(tiles, 2), (int64_t)S);  // whole 64-token steps
     p.tiles_hint = (int)(per > 0x7FFF ? 0x7FFF : per);
   }
   p.max_pages = max_pages;

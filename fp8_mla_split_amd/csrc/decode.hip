@@ -331,6 +331,7 @@ void decode_kernel(const DecodeParams p) {
   const int pt_hint = ptrow[(uint32_t)min((int)fast_div((uint32_t)(s * p.tiles_hint), p.div_tpp),
                                           p.max_pages - 1)];
   int L = seq_lens[b];
+  asm volatile("" ::"s"(L), "s"(pt_hint));  // both loads go out before either is waited for
   const int Lmax = p.max_pages * p.page_size;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int ntiles_all = (L + kTile - 1) / kTile;
@@ -340,7 +341,6 @@ void decode_kernel(const DecodeParams p) {
   const int ntiles = max(min(t_begin + per, ntiles_all) - t_begin, 0);
 
   const int64_t prow = (int64_t)(b * S + s) * M;  // first partial row of this (b, s)
-  asm volatile("" ::"s"(pt_hint));  // (issued above; consumed so that it stays)
   if (ntiles == 0) {
     wait_vmcnt<0>();  // the Q DMA lands before the workgroup's LDS is released
     for (int i = threadIdx.x; i < kRows; i += 256)
@@ -352,7 +352,10 @@ void decode_kernel(const DecodeParams p) {
   const int R = wrow0 + n;  // this lane's query row (score, P and O layout)
   const bool row_ok = R < M;
   // last visible position of the row (bottom-right causal); rows past M are never stored
-  const int lim = row_ok ? L - p.q_tokens + (int)fast_div((uint32_t)R, p.div_heads) : 0x7FFFFFFF;
+  // (computed for every lane, then selected: a branch here would make the compiler spill
+  // around it and wait for the Q DMA)
+  const int lim_r = L - p.q_tokens + (int)fast_div((uint32_t)R, p.div_heads);
+  const int lim = row_ok ? lim_r : 0x7FFFFFFF;
   const int lim_min = L - p.q_tokens + (int)fast_div((uint32_t)wrow0, p.div_heads);
   const int nsteps = (ntiles + 1) / 2;
   // Steps 0 .. nplain-1 need no masking: both tiles in the chunk and every position visible

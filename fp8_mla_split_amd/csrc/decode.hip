@@ -95,18 +95,21 @@ __device__ __forceinline__ int perm_row(int m) {
 // Index along M held in register r of a 32x32 MFMA result by lanes of half gg.
 __device__ __forceinline__ int tok_of(int gg, int r) { return 8 * (r >> 2) + 4 * gg + (r & 3); }
 
-// 16 bytes per lane, global -> LDS at M0 + 16 * lane, with M0 = lds_addr + IMM (the
-// constant part of the address stays out of the register file).  One wait state separates
-// the M0 write from the DMA that reads it.
+// M0 = a + IMM: the LDS base of the DMA instructions that follow (with one wait state before
+// the first of them).
 template <int IMM>
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff,
-                                      __amdgpu_buffer_rsrc_t rsrc) {
-  asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc), "n"(IMM)
-               : "memory", "m0", "scc");
+__device__ __forceinline__ void set_m0(uint32_t a) {
+  asm volatile("s_add_u32 m0, %0, %1\n\ts_nop 0" ::"s"(a), "n"(IMM) : "memory", "m0", "scc");
 }
-// As dma16, with the constant part in an SGPR.
+// One LDS DMA to M0 + OFF + 16 * lane from buffer offset voff + OFF (the instruction offset
+// moves the LDS destination and the global source alike, and counts in the range check).
+template <int OFF>
+__device__ __forceinline__ void dma16_at(uint32_t voff, __amdgpu_buffer_rsrc_t rsrc) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen offset:%2 lds" ::"v"(voff), "s"(rsrc), "n"(OFF)
+               : "memory");
+}
+// 16 bytes per lane, global -> LDS at M0 + 16 * lane, with M0 = lds_addr + off (one wait
+// state separates the M0 write from the DMA that reads it).
 __device__ __forceinline__ void dma16_s(uint32_t lds_addr, uint32_t voff,
                                         __amdgpu_buffer_rsrc_t rsrc, uint32_t off) {
   asm volatile("s_add_u32 m0, %0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -370,17 +373,23 @@ void decode_kernel(const DecodeParams p) {
   // page-table entry of the chunk's last tile
   const int pe_last = (int)fast_div((uint32_t)(t_begin + ntiles - 1), p.div_tpp);
 
-  // ---- DMA lane offsets.  Of a tile's 19 DMA instructions, wave w issues k = w + 4 i
-  // (i < 4, and i = 4 for waves 0..2): LDS bytes 1024 w + 4096 i of the slot.  Chunk
-  // pch = 64k + lane of the tile is row pch / 37, 16-byte column pch % 37 of the LDS tile;
+  // ---- DMA lane offsets.  Of a tile's 19 one-KiB DMA chunks (LDS bytes 1024 c of the tile
+  // slot), wave w moves chunks 4w .. 4w+3 with one M0 and instruction offsets 0, 1, 2, 3 KiB,
+  // and waves 0..2 also chunk 16 + w.  The instruction offset moves the global source like the
+  // LDS destination, so the lane offsets subtract it; tile resources start kPre bytes before
+  // the tile (and reach kPre bytes further) so that every lane offset stays non-negative.
+  // Lane l of chunk c is row (64c + l) / 37, 16-byte column (64c + l) % 37 of the LDS tile;
   // column 36 is the pad (it receives the next row's first 16 bytes, or zeros).
+  constexpr uint32_t kPre = 128;
   uint32_t voff[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) {
-    const uint32_t pch = 64u * (uint32_t)(wave + 4 * i) + (uint32_t)lane;
+    const uint32_t c = i < 4 ? 4u * (uint32_t)wave + (uint32_t)i : 16u + (uint32_t)wave;
+    const uint32_t pch = 64u * c + (uint32_t)lane;
     const uint32_t row = pch / 37u;
-    voff[i] = 16u * (pch - row);
+    voff[i] = 16u * (pch - row) + kPre - (i < 4 ? 1024u * (uint32_t)i : 0u);
   }
+  const uint32_t m0_main = 4096u * (uint32_t)wave, m0_extra = 16384u + 1024u * (uint32_t)wave;
 
   // ---- page cursor: page-table entry and tile-within-page of tile 2j of the next step j
   // to prepare, advanced two tiles per step without divisions.  With an even number of tiles
@@ -429,7 +438,8 @@ void decode_kernel(const DecodeParams p) {
     return r;
   };
   auto make_rsrc = [&](const uint8_t* base, int nrec) __attribute__((always_inline)) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nrec, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base - kPre), 0, nrec + (int)kPre,
+                                             0x00020000);
   };
   auto tile_base = [&](int page, int po) __attribute__((always_inline)) -> const uint8_t* {
     if constexpr (kPairPages)  // page_bytes < 2^32: a 32 x 32 -> 64-bit product
@@ -450,10 +460,18 @@ void decode_kernel(const DecodeParams p) {
       rb = make_rsrc(tile_base(sp.page_b, sp.po_b), tile_bytes(2 * st + 1));
   };
   // DMA instructions i of tile slot j of a step slot (i = 4 only on waves 0..2)
+  // (slot_lds: LDS address of the step slot; the two tiles of a step follow each other)
   auto tile_dma = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t slot_lds, auto jc, auto ic)
       __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value, i = decltype(ic)::value;
-    if (i < 4 || wave < 3) dma16<j * kSlot + i * 4096>(slot_lds, voff[i], rsrc);
+    if constexpr (i == 0) set_m0<j * kSlot>(slot_lds + m0_main);
+    if constexpr (i < 4) dma16_at<1024 * i>(voff[i], rsrc);
+    if constexpr (i == 4) {
+      if (wave < 3) {
+        set_m0<j * kSlot>(slot_lds + m0_extra);
+        dma16_at<0>(voff[4], rsrc);
+      }
+    }
   };
   auto issue_tile = [&](__amdgpu_buffer_rsrc_t rsrc, uint32_t slot_lds, auto jc)
       __attribute__((always_inline)) {
@@ -467,7 +485,7 @@ void decode_kernel(const DecodeParams p) {
   // into a free slot), so the number of DMA instructions in flight behind any step is fixed
   // and every wait below is a constant.
   auto slot_of = [&](int st) __attribute__((always_inline)) -> uint32_t {
-    return wave_lds + (uint32_t)((st % kStepSlots) * 2 * kSlot);
+    return lds_base + (uint32_t)((st % kStepSlots) * 2 * kSlot);
   };
   auto issue_step = [&](int st, const StepPages& sp) __attribute__((always_inline)) {
     __amdgpu_buffer_rsrc_t ra, rb;

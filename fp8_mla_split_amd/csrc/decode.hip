@@ -450,14 +450,23 @@ void decode_kernel(const DecodeParams p) {
              (uint32_t)po * (uint32_t)(kTile * kD);
   };
   // buffer resources of the two tiles of step st
-  auto step_rsrc = [&](int st, const StepPages& sp, __amdgpu_buffer_rsrc_t& ra,
-                       __amdgpu_buffer_rsrc_t& rb) __attribute__((always_inline)) {
+  // (in two halves, tile a then tile b, so that a pipeline stage can spread them over gaps)
+  auto step_rsrc_a = [&](int st, const StepPages& sp, __amdgpu_buffer_rsrc_t& ra)
+      __attribute__((always_inline)) -> const uint8_t* {
     const uint8_t* base_a = tile_base(sp.page_a, sp.po_a);
     ra = make_rsrc(base_a, tile_bytes(2 * st));
+    return base_a;
+  };
+  auto step_rsrc_b = [&](int st, const StepPages& sp, const uint8_t* base_a,
+                         __amdgpu_buffer_rsrc_t& rb) __attribute__((always_inline)) {
     if constexpr (kPairPages)
       rb = make_rsrc(base_a + kTile * kD, tile_bytes(2 * st + 1));
     else
       rb = make_rsrc(tile_base(sp.page_b, sp.po_b), tile_bytes(2 * st + 1));
+  };
+  auto step_rsrc = [&](int st, const StepPages& sp, __amdgpu_buffer_rsrc_t& ra,
+                       __amdgpu_buffer_rsrc_t& rb) __attribute__((always_inline)) {
+    step_rsrc_b(st, sp, step_rsrc_a(st, sp, ra), rb);
   };
   // DMA instructions i of tile slot j of a step slot (i = 4 only on waves 0..2)
   // (slot_lds: LDS address of the step slot; the two tiles of a step follow each other)
@@ -656,18 +665,17 @@ void decode_kernel(const DecodeParams p) {
     i32x8 kf[18];
     i32x2 va[16][4];
     __amdgpu_buffer_rsrc_t ra, rb;
-    if constexpr (kQK) {
-      kf[0] = read_k(sbk, 0);
-      kf[1] = read_k(sbk, 1);
-    }
+    const uint8_t* base_next;
+    // K fragment of the first QK (the second follows behind the first MFMA, unless the stage
+    // opens with QK)
+    if constexpr (kQK) kf[0] = read_k(sbk, 0);
+    if constexpr (kQK && !kPV) kf[1] = read_k(sbk, 1);
     if constexpr (kPV) {
       va[0][0] = vnext[0];
       va[0][1] = vnext[1];
       va[0][2] = vnext[2];
       va[0][3] = vnext[3];
     }
-    // resources of the two tiles of step st + 2 (its DMA goes into the slot step st - 2 left)
-    step_rsrc(st + 2, sp_next, ra, rb);
     // work between MFMA number G and the next one
     auto gap = [&](auto gc) __attribute__((always_inline)) {
       constexpr int G = decltype(gc)::value;
@@ -680,7 +688,14 @@ void decode_kernel(const DecodeParams p) {
       // the ten DMA instructions (five per tile), one per gap from the stage's first MFMA on:
       // the slot they fill was released by the previous stage's barrier, and the sooner they
       // are issued the more of the stage hides their HBM latency before the wait at its end
-      constexpr auto dma_gap = [](int i) { return i; };
+      constexpr auto dma_gap = [](int i) { return i + 1; };
+      // behind the stage's first MFMA: the second K fragment and the resource of tile a of
+      // step st + 2 (whose DMA goes into the slot step st - 2 left); tile b's three gaps on
+      if constexpr (G == 0) {
+        if constexpr (kQK && kPV) kf[1] = read_k(sbk, 1);
+        base_next = step_rsrc_a(st + 2, sp_next, ra);
+      }
+      if constexpr (G == 3) step_rsrc_b(st + 2, sp_next, base_next, rb);
       if constexpr (G == dma_gap(0)) tile_dma(ra, slot2, I0{}, I0{});
       if constexpr (G == dma_gap(1)) tile_dma(ra, slot2, I0{}, I1{});
       if constexpr (G == dma_gap(2)) tile_dma(ra, slot2, I0{}, I2{});
@@ -691,11 +706,11 @@ void decode_kernel(const DecodeParams p) {
       if constexpr (G == dma_gap(7)) tile_dma(rb, slot2, I1{}, I2{});
       if constexpr (G == dma_gap(8)) tile_dma(rb, slot2, I1{}, I3{});
       if constexpr (G == dma_gap(9)) tile_dma(rb, slot2, I1{}, I4{});
-      static_assert(9 < nmf, "every DMA instruction has a gap");
-      // softmax pieces k with floor(k * nmf / kPieces) == G
+      static_assert(10 < nmf, "every DMA instruction has a gap");
+      // softmax pieces k with 1 + floor(k (nmf - 1) / kPieces) == G (gap 0 holds the address work)
       static_for<kPieces>([&](auto kc) __attribute__((always_inline)) {
         constexpr int k = decltype(kc)::value;
-        if constexpr ((k * nmf) / kPieces == G) softmax_piece(sc, st, masked, k, pn);
+        if constexpr (1 + (k * (nmf - 1)) / kPieces == G) softmax_piece(sc, st, masked, k, pn);
       });
       sched_fence();
     };
@@ -705,18 +720,18 @@ void decode_kernel(const DecodeParams p) {
       if constexpr (slot_is_qk(slot)) {
         if constexpr (kQK) {
           constexpr int q = slot >= 48 ? slot - 32 : slot / 3;  // 0..17
-          if constexpr (q + 2 < 18) kf[q + 2] = read_k(sbk, q + 2);
           if constexpr (q == 0) sn.a = mfma_qk_first(kf[q], qf[0]);
           else if constexpr (q == 1) sn.b = mfma_qk_first(kf[q], qf[0]);
           else if constexpr ((q & 1) != 0) mfma_qk(sn.b, kf[q], qf[q >> 1]);
           else mfma_qk(sn.a, kf[q], qf[q >> 1]);
+          // every fragment read follows the MFMA before it, so the MFMA issues first
+          if constexpr (q + 2 < 18) kf[q + 2] = read_k(sbk, q + 2);
           gap(std::integral_constant<int, G>{});
         }
       } else {
         if constexpr (kPV) {
           constexpr int d = slot / 3;
           constexpr bool hi = slot % 3 == 0;
-          if constexpr (hi && d + 1 < 16) read_v(sbv, d + 1, va[d + 1]);
           VFrag vf;
           vf.h[0] = va[d][0];
           vf.h[1] = va[d][1];
@@ -725,6 +740,7 @@ void decode_kernel(const DecodeParams p) {
           if constexpr (hi && d == 0) mfma_pv<true>(o[d], vf.v, pp.pb.hi, escale);
           else if constexpr (hi) mfma_pv<false>(o[d], vf.v, pp.pb.hi, escale);
           else mfma_pv<false>(o[d], vf.v, pp.pb.lo, escale);
+          if constexpr (hi && d + 1 < 16) read_v(sbv, d + 1, va[d + 1]);
           gap(std::integral_constant<int, G>{});
         }
       }

@@ -220,8 +220,14 @@ def cpu_baseline(key, budget_s):
 
 
 def decode_source_hash():
-    with open(os.path.join(ROOT, "fp8_mla_split_amd", "csrc", "decode.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of decode.hip without its // comments and blank space, so that the record
+    of counters survives comment edits but not code changes (the source has no "//" inside
+    string literals)."""
+    import re
+    with open(os.path.join(ROOT, "fp8_mla_split_amd", "csrc", "decode.hip")) as f:
+        code = re.sub(r"//[^\n]*", "", f.read())
+    code = "\n".join(" ".join(line.split()) for line in code.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload):

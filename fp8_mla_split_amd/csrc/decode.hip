@@ -18,16 +18,18 @@
 // KV staging.  A tile is 32 tokens x 576 bytes; a step is two tiles (64 tokens).  Tiles go
 // HBM -> LDS with buffer_load ... lds (16 bytes per lane, no VGPR round trip) into an
 // 8-tile ring (152 KiB of the CU's 160 KiB) = 4 step slots.  While the waves work on steps
-// i and i + 1, steps i + 2 and i + 3 are in flight.  Rows are stored with a 592-byte pitch
-// (37 x 16 B); the 64-bank LDS then serves both read patterns below without conflicts.
+// i - 1, i and i + 1 (see Schedule), step i + 2 is in flight.  Rows are stored with a
+// 592-byte pitch (37 x 16 B); the 64-bank LDS then serves both read patterns below without
+// conflicts.
 // The buffer resource of each tile is bounded by the number of valid rows, so rows past
 // the end of the sequence arrive as zeros: no NaN bytes from a page's unused tail can reach
 // the P.V product (0 x NaN).  The query rows are staged through the same ring (in its last
 // four tile slots, before the ring starts) and then held in registers.  Every DMA is issued
 // from inline asm and waited on with explicit vmcnt counts: the compiler does not track
-// them, so none of its own waits drain the ring, and the kernel issues no compiler-visible
-// global load before the main loop for the same reason.  M0 is written only by these asm
-// statements (the compiler uses it for nothing else in this kernel).
+// them, so none of its own waits drain the ring (vector memory operations of its own, such
+// as a register spill in the set-up, only make those counts wait longer, never shorter,
+// since they complete in order).  M0 is written only by these asm statements (the compiler
+// uses it for nothing else in this kernel).
 //
 // Math per step (per wave, 32 rows x 64 tokens), all on FP8 MFMA v_mfma_scale_f32_32x32x64:
 //  * S^T = K . Q^T per tile: tokens along M, rows along N, 576 = 9 x 64 channels along K;
@@ -50,14 +52,16 @@
 //    value columns, so the epilogue stores 8 bytes per lane and instruction.
 //  * V (the first 512 columns of the same tiles) is read transposed with ds_read_b64_tr_b8.
 //
-// Schedule.  One wave issues at most one instruction every ~4 clocks and an MFMA runs 64
-// clocks, so about a dozen other instructions fit behind each MFMA.  A step's 50 MFMAs are
-// therefore interleaved with all of the step's other work in near-equal shares: the 18 QK
-// MFMAs of step i+1 carry the K fragment reads, the hi/lo encoding of step i's
-// probabilities and the DMA of step i+3; the 32 PV MFMAs of step i carry the V fragment
-// reads and the max / exp2 / sum of step i+1's scores.  The per-step barrier follows the
-// last PV MFMA, so the matrix pipe keeps working through it.  Masking (sequence tail,
-// causal positions, tiles past the chunk) is a uniform branch taken only in the last steps.
+// Schedule.  A lone wave issues its instructions in order, and an MFMA keeps the matrix pipe
+// busy for 64 clocks while the wave issues others behind it (measured: about eight VALU
+// instructions, fewer transcendental, conversion or scalar ones).  Stage i of the pipeline
+// runs the QK MFMAs of step i + 1, the softmax of step i and the P.V MFMAs of step i - 1,
+// which are independent, interleaved as (PV hi, PV lo, QK) x 16, QK, QK: 50 MFMAs with all
+// other work of the stage split into small pieces between them - fragment reads one or two
+// MFMAs ahead of use, the address work and 10 DMA instructions of step i + 2 near the start,
+// the softmax pieces over the rest.  One vmcnt wait and a barrier end the stage, after its
+// last MFMA has issued.  Masking (sequence tail, causal positions, tiles past the chunk) is
+// a uniform branch taken only in the last steps.
 #include <type_traits>
 #include <utility>
 
@@ -85,8 +89,6 @@ constexpr int kRows = 128;                  // query rows per workgroup
 constexpr float kHeadroom = 64.0f;          // log2 range of a pass above its reference max
 constexpr float kLog2PScale = 7.807354922057604f;  // log2(224): p in [0, 448)
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kKAhead = 2;                  // QK MFMA pairs whose K fragments are in flight
-constexpr int kVAhead = 2;                  // PV blocks whose V fragments are in flight
 
 // MFMA token index -> LDS row of the tile: bits (b4 b3 b2 b1 b0) -> (b4 b3 b1 b0 b2).
 __device__ __forceinline__ int perm_row(int m) {

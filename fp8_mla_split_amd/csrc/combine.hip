@@ -210,10 +210,12 @@ static void launch_batch(const uint16_t* po, const float* pl, int batch, int spl
 
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
                           float v_scale, uint16_t* out, float* out_lse, hipStream_t s) {
-  // as many loads in flight per wave as there are splits to cover, up to 16
+  // As many loads in flight per wave as there are splits to cover, up to 16; from 64 splits
+  // on, 8 per wave and twice the waves (up to 16) spread the loads wider (measured on MI355X:
+  // 6.2 instead of 6.5 us at 256 splits, 3.9 instead of 4.4 at 64).
   if (splits <= 4 * kCw)
     launch_batch<4>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
-  else if (splits <= 8 * kCw)
+  else if (splits <= 8 * kCw || splits >= 64)
     launch_batch<8>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
   else
     launch_batch<16>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);

@@ -17,6 +17,9 @@ Prints one JSON line.  `value` is microseconds per decode step on the batch-1, 1
 workload; the batch-16 workload is reported alongside.  `roofline` is for the decode kernel
 (HBM-bound at one query token per request): algorithmic bytes = KV bytes + Q bytes per
 launch (576 B per cached token, 576 B per query row), divided by its average duration.
+`extras` (skipped with --no-extras) holds reference rates measured in the same run (a
+streaming HBM read, a device copy, KV-sized quantisation), p10/p50/p90 of single timed
+steps, and decode + combine time over a sweep of split counts beside the planner's choice.
 """
 from __future__ import annotations
 
@@ -51,6 +54,8 @@ def _parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying graphs "
                          "(what a profiler run needs to see individual launches clearly)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the HBM probes, per-step percentiles and the split sweep")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, --steps times (the "
                          "reference kernel that calibrates HBM byte counters), then exit")
@@ -184,6 +189,148 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
     return res
 
 
+def _time_fn_graph(fn, n, reps=3):
+    """Microseconds per call of fn, n calls captured in one HIP graph, reps replays."""
+    import torch
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(n):
+            fn()
+    g.replay()
+    return _time_graph(g, reps) * 1e3 / n
+
+
+def hbm_probes():
+    """Measured HBM rates in this run, on the GPU the decode ran on: a streaming read of 1 GiB
+    through the library's read probe (and torch's sum over it, for comparison), a device copy
+    of 1 GiB (read + write), and the KV-sized
+    saturating quantisation through this library (a 2^28-element fp32 tensor, 4 B read + 1 B
+    written per element).  These are reference rates, not part of the timed step."""
+    import torch
+    import fp8_mla_split_amd as mla
+    n = 1 << 28
+    x = torch.randn(n, device="cuda")
+    y = torch.empty_like(x)
+    q8 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    acc = torch.empty((), device="cuda")
+
+    def timed(fn, reps=10):  # eager launches: each moves 1-5 GiB, launch gaps are noise
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    read_us = timed(lambda: mla.hbm_read_probe(x, sink, 2048))
+    sum_us = timed(lambda: torch.sum(x, dim=(0,), out=acc))
+    copy_us = timed(lambda: y.copy_(x))
+    quant_us = timed(lambda: mla.quantize_fp8_sat(x, 0.01, out=q8))
+    res = {"read_gbps": round(4 * n / (read_us * 1e3), 1),
+           "torch_sum_read_gbps": round(4 * n / (sum_us * 1e3), 1),
+           "copy_gbps": round(8 * n / (copy_us * 1e3), 1),
+           "kv_quantize_gbps": round(5 * n / (quant_us * 1e3), 1),
+           "kv_quantize_us_per_gi_element": round(quant_us * 4, 1)}
+    res["kv_quantize_frac_of_hbm_peak"] = round(res["kv_quantize_gbps"] / HBM_PEAK_GBPS, 4)
+    del x, y, q8
+    torch.cuda.empty_cache()
+    return res
+
+
+def step_percentiles(key, n_steps=60):
+    """p10 / p50 / p90 of single decode steps (quantize + decode + combine), each a one-step
+    HIP graph on its own KV copy (so no step finds its KV cached), timed with events."""
+    import torch
+    import fp8_mla_split_amd as mla
+    from fp8_mla_split_amd.workload import materialize
+    from synthetic import WORKLOADS, q_f32
+
+    w = WORKLOADS[key]
+    dw = materialize(w)
+    kv_bytes = dw.kv_tokens * 576
+    copies = max(2, -(-(512 << 20) // max(kv_bytes, 1)) + 1) if kv_bytes < (512 << 20) else 2
+    pools = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(copies - 1)]
+    q32 = torch.from_numpy(q_f32(w)).cuda()
+    q8 = torch.empty_like(q32, dtype=torch.uint8)
+    plan = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len)
+    S = plan.num_splits
+    po = torch.empty((w.batch, S, w.q_tokens * w.heads, 512), dtype=torch.float16, device="cuda")
+    pl = torch.empty((w.batch, S, w.q_tokens * w.heads), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.batch, w.q_tokens, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    graphs = []
+    for i in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            mla.quantize_fp8_sat(q32, dw.q_scale, out=q8)
+            mla.decode_splitkv(q8, pools[i], dw.page_table, dw.seq_lens, dw.q_scale, dw.kv_scale,
+                               w.softmax_scale, dw.max_seq_len, S, 0, po, pl)
+            mla.splitkv_combine(po, pl, w.q_tokens, w.heads, dw.kv_scale, out=out)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    with torch.cuda.stream(stream):
+        for k in range(n_steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graphs[k % copies].replay()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+    p10, p50, p90 = np.percentile(ts, [10, 50, 90])
+    del graphs, pools, dw
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "steps": n_steps, "p10_us": round(float(p10), 2),
+            "p50_us": round(float(p50), 2), "p90_us": round(float(p90), 2),
+            "note": "one-step graph replays, each launched and timed on its own (includes "
+                    "the graph launch latency that back-to-back steps overlap)"}
+
+
+def split_sweep(key, splits=(8, 16, 32, 64, 128, 256, 512), n=40):
+    """Decode + combine time at fixed split counts beside the planner's choice (graph-timed,
+    KV copies rotated as in the main measurement)."""
+    import torch
+    import fp8_mla_split_amd as mla
+    from fp8_mla_split_amd.workload import materialize
+    from synthetic import WORKLOADS
+
+    w = WORKLOADS[key]
+    dw = materialize(w)
+    kv_bytes = dw.kv_tokens * 576
+    copies = max(1, -(-(512 << 20) // max(kv_bytes, 1)) + 1) if kv_bytes < (512 << 20) else 1
+    pools = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(copies - 1)]
+    plan = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len)
+    rows = []
+    for S in sorted(set(splits) | {plan.num_splits}):
+        po = torch.empty((w.batch, S, w.q_tokens * w.heads, 512), dtype=torch.float16,
+                         device="cuda")
+        pl = torch.empty((w.batch, S, w.q_tokens * w.heads), dtype=torch.float32, device="cuda")
+        out = torch.empty((w.batch, w.q_tokens, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+        it = [0]
+
+        def one():
+            mla.decode_splitkv(dw.q8, pools[it[0] % copies], dw.page_table, dw.seq_lens,
+                               dw.q_scale, dw.kv_scale, w.softmax_scale, dw.max_seq_len, S, 0,
+                               po, pl)
+            mla.splitkv_combine(po, pl, w.q_tokens, w.heads, dw.kv_scale, out=out)
+            it[0] += 1
+        us = _time_fn_graph(one, n)
+        rows.append({"splits": S, "decode_plus_combine_us": round(us, 2),
+                     "planner": S == plan.num_splits})
+        del po, pl, out
+    del pools, dw
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "rows": rows}
+
+
 def cpu_baseline(key, budget_s):
     """The oracle as it stands, one decode step at a time on the host cores, until about
     budget_s seconds of work are done (the sample is a count of whole steps of request 0)."""
@@ -271,6 +418,19 @@ def main():
         print(f"[bench] {a.also}: {also['us_per_step']:.2f} us/step (decode "
               f"{also['decode_us']:.2f} us, {also['decode_gbps']:.0f} GB/s)",
               file=sys.stderr, flush=True)
+    extras = None
+    if not a.no_extras:
+        extras = {"hbm_probes": hbm_probes(),
+                  "step_percentiles": step_percentiles(a.workload),
+                  "split_sweep": split_sweep(a.workload)}
+        pr = extras["hbm_probes"]
+        print(f"[bench] measured HBM: read {pr['read_gbps']:.0f} GB/s, copy {pr['copy_gbps']:.0f} "
+              f"GB/s, KV quantize {pr['kv_quantize_gbps']:.0f} GB/s; step p10/p50/p90 "
+              f"{extras['step_percentiles']['p10_us']}/{extras['step_percentiles']['p50_us']}/"
+              f"{extras['step_percentiles']['p90_us']} us", file=sys.stderr, flush=True)
+        print("[bench] split sweep: " + ", ".join(
+            f"S={r['splits']}{'*' if r['planner'] else ''} {r['decode_plus_combine_us']:.1f} us"
+            for r in extras["split_sweep"]["rows"]), file=sys.stderr, flush=True)
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(a.workload, a.cpu_seconds)
@@ -304,6 +464,9 @@ def main():
                      "mfma_tflops_algorithmic": round(main_res["decode_mfma_tflops_algorithmic"], 1),
                      "mfma_peak_tflops_fp8": FP8_PEAK_TFLOPS},
         "cpu_baseline": cpu,
+        "decode_frac_of_measured_read_peak": None if extras is None else round(
+            achieved / extras["hbm_probes"]["read_gbps"], 4),
+        "extras": extras,
         "also": None if also is None else {
             "workload": also["workload"], "us_per_step": round(also["us_per_step"], 3),
             "decode_us": round(also["decode_us"], 3),

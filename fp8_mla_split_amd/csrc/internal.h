@@ -53,6 +53,9 @@ struct DecodeParams {
 
 hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scale, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t s);
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int grid,
+                             hipStream_t s);
+int64_t read_probe_chunk_bytes();
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
                           float v_scale, uint16_t* out, float* out_lse, hipStream_t s);
 

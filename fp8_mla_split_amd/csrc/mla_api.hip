@@ -194,4 +194,14 @@ mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* parti
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+mla_status mla_hbm_read_probe(const void* buf_dev, int64_t bytes, uint32_t* out_dev,
+                              int grid, void* stream) {
+  if (buf_dev == nullptr || out_dev == nullptr || grid < 1 || bytes < 0 ||
+      bytes % mla::read_probe_chunk_bytes() != 0 || ((uintptr_t)buf_dev & 15) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (bytes == 0) return MLA_OK;
+  const hipError_t e = mla::launch_read_probe(buf_dev, bytes, out_dev, grid, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 }  // extern "C"

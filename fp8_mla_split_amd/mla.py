@@ -33,6 +33,8 @@ _lib.mla_decode_splitkv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, 
                                     _f32, _f32, _f32, _i32, _i32, _vp, _vp, _i64, _vp]
 _lib.mla_splitkv_combine.restype = _i32
 _lib.mla_splitkv_combine.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]
+_lib.mla_hbm_read_probe.restype = _i32
+_lib.mla_hbm_read_probe.argtypes = [_vp, _i64, _vp, _i32, _vp]
 
 D_KV, D_V = 576, 512
 
@@ -156,6 +158,15 @@ def splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens
                                     float(v_scale), _ptr(out), _ptr(out_lse), _stream(dev)),
            "mla_splitkv_combine")
     return out, out_lse
+
+
+def hbm_read_probe(buf: torch.Tensor, out: torch.Tensor, grid: int) -> None:
+    """Diagnostics: stream every byte of buf (a multiple of 32 KiB) from HBM; one uint32
+    XOR-fold per workgroup into out[:grid].  Used to measure the read rate in benchmarks."""
+    if not buf.is_cuda or not out.is_cuda or out.dtype != torch.int32 or out.numel() < grid:
+        raise ValueError("buf and out must be device tensors, out int32 with >= grid elements")
+    _check(_lib.mla_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                   int(grid), _stream(buf.device)), "mla_hbm_read_probe")
 
 
 def decode(q8, kv_pool8, page_table, seq_lens, q_scale, kv_scale, softmax_scale, max_seq_len,

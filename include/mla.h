@@ -149,6 +149,19 @@ mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* parti
                                int batch, int num_splits, int q_tokens, int heads, float v_scale,
                                uint16_t* out_bf16_dev, float* out_lse_dev, void* stream);
 
+/*
+ * Diagnostics, not part of the decode path: streams bytes of buf_dev from HBM (16-byte
+ * non-temporal loads, eight in flight per lane) and writes one XOR-fold word per workgroup
+ * to out_dev[0 .. grid-1].  Benchmarks time it to state the read rate the decode kernel's KV
+ * traffic is compared with, on the same GPU in the same run.
+ *   buf_dev  device buffer, 16-byte aligned; bytes a multiple of 32 KiB (>= 0);
+ *   out_dev  uint32 [grid] (device); grid >= 1 workgroups of 256 lanes.
+ * Errors: INVALID_ARG (NULL pointers, misalignment, bytes not a multiple of 32 KiB, grid < 1);
+ * HIP.  bytes == 0 enqueues nothing.
+ */
+mla_status mla_hbm_read_probe(const void* buf_dev, int64_t bytes, uint32_t* out_dev, int grid,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -176,3 +176,14 @@ def test_graft_entry_build_imports_the_binding_in_a_fresh_process():
     )
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stderr[-2000:]
+
+
+def test_read_probe_rejects_bad_arguments(lib):
+    r = lib.mla_hbm_read_probe
+    r.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert r(None, 32768, FAKE, 1, None) == INVALID
+    assert r(FAKE, 32768, None, 1, None) == INVALID
+    assert r(FAKE, 32768, FAKE, 0, None) == INVALID
+    assert r(FAKE, 1000, FAKE, 1, None) == INVALID       # not a multiple of 32 KiB
+    assert r(ctypes.c_void_p(0x1004), 32768, FAKE, 1, None) == INVALID  # not 16-byte aligned
+    assert r(FAKE, 0, FAKE, 1, None) == OK                # nothing to read

@@ -91,3 +91,16 @@ def test_outlier_workload_saturates_to_448_never_nan():
     sat = np.mean((got & 0x7F) == 0x7E)
     assert 0.008 < sat < 0.012, sat             # ~1 % of values are x1000 outliers
     assert not np.any((got & 0x7F) == 0x7F)     # no NaN codes
+
+
+def test_read_probe_reads_every_byte():
+    """The benchmark's HBM read probe: its per-workgroup XOR folds, combined, equal the XOR of
+    every 32-bit word of the buffer (so it read all of it), for several grid sizes."""
+    n_words = 3 * (32768 // 4) * 5  # 15 blocks of 32 KiB
+    words = torch.randint(-2**31, 2**31 - 1, (n_words,), dtype=torch.int32, device="cuda")
+    want = np.bitwise_xor.reduce(words.cpu().numpy().view(np.uint32))
+    for grid in (1, 4, 15, 64):
+        out = torch.zeros(grid, dtype=torch.int32, device="cuda")
+        mla.hbm_read_probe(words, out, grid)
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        assert got == want, grid

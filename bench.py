@@ -174,7 +174,11 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
 
     q_bytes = B * Sq * H * 576
     algo = kv_bytes + q_bytes
-    flops = 2.0 * B * Sq * H * dw.kv_tokens * (576 + 512)  # QK^T + PV, algorithmic
+    # QK^T + PV, algorithmic: 2 * 1088 flops per (query row, cached token) of each request
+    # (kv_tokens already sums the requests' lengths); the kernel executes 50 FP8 MFMAs of
+    # 32x32x64 per 32 rows x 64 tokens (P.V twice, hi and lo): 3200 flops per (row, token)
+    flops = 2.0 * Sq * H * dw.kv_tokens * (576 + 512)
+    flops_exec = 3200.0 * Sq * H * dw.kv_tokens
     res.update({
         "us_per_step": step_us,
         "quantize_q_us": q_us, "decode_us": dec_us, "combine_us": comb_us,
@@ -182,6 +186,7 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
         "decode_gbps": algo / (dec_us * 1e3),
         "step_kv_gbps": kv_bytes / (step_us * 1e3),
         "decode_mfma_tflops_algorithmic": flops / (dec_us * 1e6),
+        "decode_mfma_tflops_executed": flops_exec / (dec_us * 1e6),
         "partial_bytes": B * S * Sq * H * (512 * 2 + 4),
     })
     del pools, po, pl, dw
@@ -462,6 +467,7 @@ def main():
                      "kernel": "decode_kernel (mla_decode_splitkv)",
                      "algorithmic_bytes_per_launch": main_res["algo_bytes_decode"],
                      "mfma_tflops_algorithmic": round(main_res["decode_mfma_tflops_algorithmic"], 1),
+                     "mfma_tflops_executed": round(main_res["decode_mfma_tflops_executed"], 1),
                      "mfma_peak_tflops_fp8": FP8_PEAK_TFLOPS},
         "cpu_baseline": cpu,
         "decode_frac_of_measured_read_peak": None if extras is None else round(
@@ -474,6 +480,10 @@ def main():
             "decode_gbps": round(also["decode_gbps"], 1),
             "decode_frac_of_hbm_peak": round(also["decode_gbps"] / HBM_PEAK_GBPS, 4),
             "step_kv_gbps": round(also["step_kv_gbps"], 1),
+            "decode_mfma_tflops_algorithmic": round(also["decode_mfma_tflops_algorithmic"], 1),
+            "decode_mfma_tflops_executed": round(also["decode_mfma_tflops_executed"], 1),
+            "decode_mfma_frac_of_fp8_peak_executed": round(
+                also["decode_mfma_tflops_executed"] / FP8_PEAK_TFLOPS, 4),
             "num_splits": also["num_splits"], "rows_per_group": also["rows_per_group"]},
         "detail": main_res,
         "wall_s": round(time.time() - t_wall, 1),

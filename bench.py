@@ -104,7 +104,7 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
     pools = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(copies - 1)]
     q32 = torch.from_numpy(q_f32(w)).cuda()
     q8 = torch.empty_like(q32, dtype=torch.uint8)
-    plan = mla.splitkv_plan(B, Sq, H, dw.max_seq_len)
+    plan = mla.splitkv_plan(B, Sq, H, dw.max_seq_len, total_kv_tokens=dw.kv_tokens)
     S = splits or plan.num_splits
     r = rows_per_group or plan.rows_per_group
     po = torch.empty((B, S, Sq * H, 512), dtype=torch.float16, device="cuda")
@@ -262,7 +262,8 @@ def step_percentiles(key, n_steps=60):
     pools = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(copies - 1)]
     q32 = torch.from_numpy(q_f32(w)).cuda()
     q8 = torch.empty_like(q32, dtype=torch.uint8)
-    plan = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len)
+    plan = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len,
+                            total_kv_tokens=dw.kv_tokens)
     S = plan.num_splits
     po = torch.empty((w.batch, S, w.q_tokens * w.heads, 512), dtype=torch.float16, device="cuda")
     pl = torch.empty((w.batch, S, w.q_tokens * w.heads), dtype=torch.float32, device="cuda")
@@ -312,7 +313,8 @@ def split_sweep(key, splits=(8, 16, 32, 64, 128, 256, 512), n=40):
     kv_bytes = dw.kv_tokens * 576
     copies = max(1, -(-(512 << 20) // max(kv_bytes, 1)) + 1) if kv_bytes < (512 << 20) else 1
     pools = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(copies - 1)]
-    plan = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len)
+    plan = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len,
+                            total_kv_tokens=dw.kv_tokens)
     rows = []
     for S in sorted(set(splits) | {plan.num_splits}):
         po = torch.empty((w.batch, S, w.q_tokens * w.heads, 512), dtype=torch.float16,

@@ -31,32 +31,38 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Planner cost model, in microseconds, with rates measured on MI355X for the decode kernel
 // (one workgroup per CU; a 64-token step of 128 query rows takes ~2.8 us) plus the traffic
-// of the split partials (written by the decode kernel, read back by the combine).  Every
-// request is assumed to be max_seq_len long.
+// of the split partials (written by the decode kernel, read back by the combine).  A request
+// of L tokens is cut into S chunks of ceil(ceil(L/64) / S) steps.  The hardware hands
+// workgroups to CUs as CUs free up, so the decode takes about the longer of the longest
+// chunk and the total work spread over the CUs; total_tokens (the sum of the requests'
+// lengths) is B * L_max when every request is as long as the longest.
 constexpr double kStepUs = 2.8;             // one 64-token step of one workgroup
 constexpr double kWgOverheadUs = 3.0;       // staging before the first step, epilogue
 constexpr double kPartialBytesPerUs = 5e6;  // partial rows written + read back
 constexpr double kCombineUs = 3.0;          // the combine launch itself
 
-double plan_cost(int64_t B, int64_t M, int64_t L, int cu, int64_t S) {
+double plan_cost(int64_t B, int64_t M, int64_t L, int64_t total_tokens, int cu, int64_t S) {
   const int64_t G = cdiv(M, 128);
-  const int64_t tiles = cdiv(L, 32);
-  const int64_t steps = cdiv(cdiv(tiles, 2), S);  // chunks are whole 64-token steps
+  const int64_t steps_max = cdiv(cdiv(L, 64), S);  // the longest chunk
+  const int64_t total_steps = G * cdiv(total_tokens, 64);
+  const int64_t per_cu = cdiv(total_steps, cu);
   const int64_t rounds = cdiv(B * S * G, cu);
-  const double t_dec = (double)rounds * (kWgOverheadUs + (double)steps * kStepUs);
+  const double t_dec = (double)rounds * kWgOverheadUs +
+                       (double)(steps_max > per_cu ? steps_max : per_cu) * kStepUs;
   const double t_part = (double)(B * S * M) * (1024.0 + 4.0) * 2.0 / kPartialBytesPerUs;
   return t_dec + t_part + (S > 1 ? kCombineUs : 0.0);
 }
 
-mla_status plan(int batch, int q_tokens, int heads, int max_seq_len, int cu, int* splits,
-                int* rows_per_group) {
+mla_status plan(int batch, int q_tokens, int heads, int max_seq_len, int64_t total_tokens,
+                int cu, int* splits, int* rows_per_group) {
   const int64_t M = (int64_t)q_tokens * heads;
   const int64_t tiles = cdiv(max_seq_len, 32);
   const int64_t s_max = tiles / 2 > 0 ? tiles / 2 : 1;  // at least one full step per chunk
+  const int64_t total = total_tokens > 0 ? total_tokens : (int64_t)batch * max_seq_len;
   double best = -1.0;
   int best_s = 1;
   for (int64_t S = 1; S <= s_max && S <= 4096; ++S) {
-    const double c = plan_cost(batch, M, max_seq_len, cu, S);
+    const double c = plan_cost(batch, M, max_seq_len, total, cu, S);
     if (best < 0.0 || c < best) {
       best = c;
       best_s = (int)S;
@@ -91,9 +97,11 @@ mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t 
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len, int cu_count,
-                            int* num_splits, int* rows_per_group, int64_t* partial_rows) {
-  if (batch < 1 || q_tokens < 1 || heads < 1 || max_seq_len < 1 || cu_count < 0)
+mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
+                            int64_t total_kv_tokens, int cu_count, int* num_splits,
+                            int* rows_per_group, int64_t* partial_rows) {
+  if (batch < 1 || q_tokens < 1 || heads < 1 || max_seq_len < 1 || cu_count < 0 ||
+      total_kv_tokens < 0 || total_kv_tokens > (int64_t)batch * max_seq_len)
     return MLA_ERR_INVALID_ARG;
   if ((int64_t)q_tokens * heads > mla::kMaxRows) return MLA_ERR_UNSUPPORTED;
   int cu = cu_count;
@@ -102,7 +110,7 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
     if (st != MLA_OK) return st;
   }
   int s = 1, r = 128;
-  plan(batch, q_tokens, heads, max_seq_len, cu, &s, &r);
+  plan(batch, q_tokens, heads, max_seq_len, total_kv_tokens, cu, &s, &r);
   if (num_splits) *num_splits = s;
   if (rows_per_group) *rows_per_group = r;
   if (partial_rows) *partial_rows = (int64_t)batch * s * q_tokens * heads;
@@ -137,7 +145,7 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
     const mla_status st = device_cu_count(&cu);
     if (st != MLA_OK) return st;
     int ps = 1, pr = 128;
-    plan(batch, q_tokens, heads, max_seq_len, cu, &ps, &pr);
+    plan(batch, q_tokens, heads, max_seq_len, 0, cu, &ps, &pr);
     if (S == 0) S = ps;
     if (r == 0) r = pr;
   }

@@ -26,7 +26,7 @@ _lib.mla_status_string.argtypes = [_i32]
 _lib.mla_quantize_fp8_sat.restype = _i32
 _lib.mla_quantize_fp8_sat.argtypes = [_vp, _vp, _i64, _f32, _vp]
 _lib.mla_splitkv_plan.restype = _i32
-_lib.mla_splitkv_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_i32),
+_lib.mla_splitkv_plan.argtypes = [_i32, _i32, _i32, _i32, _i64, _i32, ctypes.POINTER(_i32),
                                   ctypes.POINTER(_i32), ctypes.POINTER(_i64)]
 _lib.mla_decode_splitkv.restype = _i32
 _lib.mla_decode_splitkv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -88,9 +88,12 @@ def quantize_fp8_sat(x: torch.Tensor, scale: float, out: Optional[torch.Tensor] 
 
 
 def splitkv_plan(batch: int, q_tokens: int, heads: int, max_seq_len: int,
-                 cu_count: int = 0) -> Plan:
+                 cu_count: int = 0, total_kv_tokens: int = 0) -> Plan:
+    """Split count and row grouping; total_kv_tokens = the sum of the requests' lengths if
+    known (0: every request is max_seq_len long)."""
     s, r, n = _i32(), _i32(), _i64()
-    _check(_lib.mla_splitkv_plan(batch, q_tokens, heads, max_seq_len, cu_count,
+    _check(_lib.mla_splitkv_plan(batch, q_tokens, heads, max_seq_len, int(total_kv_tokens),
+                                 cu_count,
                                  ctypes.byref(s), ctypes.byref(r), ctypes.byref(n)),
            "mla_splitkv_plan")
     return Plan(s.value, r.value, n.value)

@@ -80,12 +80,18 @@ mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t 
  *                    which read the chunk's KV through the same L2;
  *   *partial_rows    B * S * Sq * H: the entries mla_decode_splitkv writes, i.e. the sizes
  *                    of partial_o (x 512 fp16 values) and partial_lse (x 1 float).
+ *   total_kv_tokens : the sum of the requests' lengths when the caller knows it (mixed
+ *                    lengths: the split count then balances the total work over the CUs
+ *                    against the longest request's chunks); 0 = every request is
+ *                    max_seq_len long (what mla_decode_splitkv assumes when it plans);
  *   cu_count : compute units to plan for; 0 queries the current device (a HIP call).
  * Any output pointer may be NULL.  Errors: INVALID_ARG for batch, q_tokens, heads or
- * max_seq_len < 1 or cu_count < 0; UNSUPPORTED when q_tokens * heads > 65536.
+ * max_seq_len < 1, cu_count < 0, or total_kv_tokens outside [0, batch * max_seq_len];
+ * UNSUPPORTED when q_tokens * heads > 65536.
  */
-mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len, int cu_count,
-                            int* num_splits, int* rows_per_group, int64_t* partial_rows);
+mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
+                            int64_t total_kv_tokens, int cu_count, int* num_splits,
+                            int* rows_per_group, int64_t* partial_rows);
 
 /*
  * Split-KV partial attention over an FP8 paged KV cache ([A/MLA] items (1)-(3), [B]).

@@ -29,7 +29,7 @@ def lib():
     i, f, v, i64 = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64
     L.mla_decode_splitkv.argtypes = [v, v, v, v, i, i, i, i, i, i, f, f, f, i, i, v, v, i64, v]
     L.mla_splitkv_combine.argtypes = [v, v, i, i, i, i, f, v, v, v]
-    L.mla_splitkv_plan.argtypes = [i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+    L.mla_splitkv_plan.argtypes = [i, i, i, i, i64, i, ctypes.POINTER(i), ctypes.POINTER(i),
                                    ctypes.POINTER(i64)]
     return L
 
@@ -123,9 +123,10 @@ def test_combine_rejects_bad_arguments(lib):
     assert c(None, None, 0, 4, 1, 16, 1.0, None, None, None) == OK
 
 
-def _plan(lib, B, Sq, H, L, cu):
+def _plan(lib, B, Sq, H, L, cu, total=0):
     s, r, n = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
-    st = lib.mla_splitkv_plan(B, Sq, H, L, cu, ctypes.byref(s), ctypes.byref(r), ctypes.byref(n))
+    st = lib.mla_splitkv_plan(B, Sq, H, L, total, cu, ctypes.byref(s), ctypes.byref(r),
+                              ctypes.byref(n))
     return st, s.value, r.value, n.value
 
 
@@ -134,6 +135,8 @@ def test_plan_rejects_bad_arguments(lib):
     assert _plan(lib, 1, 1, 128, 0, 256)[0] == INVALID
     assert _plan(lib, 1, 1, 128, 1000, -1)[0] == INVALID
     assert _plan(lib, 1, 2, 40000, 1000, 256)[0] == UNSUPPORTED
+    assert _plan(lib, 2, 1, 128, 1000, 256, total=-1)[0] == INVALID
+    assert _plan(lib, 2, 1, 128, 1000, 256, total=2001)[0] == INVALID   # > batch * max
 
 
 @pytest.mark.parametrize("B,Sq,H,L", [(1, 1, 128, 131072), (16, 1, 128, 131072),
@@ -158,6 +161,17 @@ def test_split_count_follows_cu_count_and_context(lib):
     assert s_128 < s_256
     assert s_short < s_256
     assert _plan(lib, 64, 1, 128, 131072, 256)[1] < s_256
+
+
+def test_plan_total_tokens(lib):
+    """Equal lengths: giving the total changes nothing.  Mixed lengths (the total well below
+    batch x the longest): more splits, so the longest request's chunks shrink toward the
+    average work per CU."""
+    for B, L in [(1, 131072), (16, 131072), (32, 131072), (4, 1048576)]:
+        assert _plan(lib, B, 1, 128, L, 256, total=B * L)[1:] == _plan(lib, B, 1, 128, L, 256)[1:]
+    s_eq = _plan(lib, 32, 1, 128, 131072, 256)[1]
+    s_mixed = _plan(lib, 32, 1, 128, 131072, 256, total=32 * 67584)[1]   # U[4K, 128K] mean
+    assert s_mixed > s_eq
 
 
 def test_graft_entry_build_imports_the_binding_in_a_fresh_process():

@@ -160,9 +160,17 @@ def test_b16_128k_sampled(full):
     _compare(dw, o, l, _oracle(dw, [0, 9, 15]))
 
 
-def test_paged_b32_sampled(full):
+@pytest.mark.parametrize("with_total", [False, True])
+def test_paged_b32_sampled(full, with_total):
+    """Planned inside the decode call (every request assumed as long as the longest), and as
+    the benchmark plans it (the requests' total length given to the planner)."""
     dw = full("paged_b32")
-    o, l, _ = _run(dw)
+    S = 0
+    if with_total:
+        w = dw.w
+        S = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len,
+                             total_kv_tokens=dw.kv_tokens).num_splits
+    o, l, _ = _run(dw, S)
     lens = dw.seq_lens_host
     picks = [int(np.argmin(lens)), int(np.argmax(lens)), 13]
     _compare(dw, o, l, _oracle(dw, picks))

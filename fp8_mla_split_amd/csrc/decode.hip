@@ -293,6 +293,8 @@ void decode_kernel(const DecodeParams p) {
                "s"(p.div_splits.s1), "s"(p.div_splits.s2), "s"(p.div_groups.m),
                "s"(p.div_groups.s1), "s"(p.div_groups.s2), "s"(p.div_tpp.m), "s"(p.div_tpp.s1),
                "s"(p.div_tpp.s2));
+  asm volatile("" ::"s"(p.kv), "s"(p.page_bytes), "s"(p.div_heads.m), "s"(p.div_heads.s1),
+               "s"(p.div_heads.s2), "s"(p.partial_o), "s"(p.partial_lse));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 31, gg = lane >> 5;
@@ -353,23 +355,6 @@ void decode_kernel(const DecodeParams p) {
     return;
   }
 
-  const int wrow0 = row0 + wave * 32;
-  const int R = wrow0 + n;  // this lane's query row (score, P and O layout)
-  const bool row_ok = R < M;
-  // last visible position of the row (bottom-right causal); rows past M are never stored
-  // (computed for every lane, then selected: a branch here would make the compiler spill
-  // around it and wait for the Q DMA)
-  const int lim_r = L - p.q_tokens + (int)fast_div((uint32_t)R, p.div_heads);
-  const int lim = row_ok ? lim_r : 0x7FFFFFFF;
-  const int lim_min = L - p.q_tokens + (int)fast_div((uint32_t)wrow0, p.div_heads);
-  const int nsteps = (ntiles + 1) / 2;
-  // Steps 0 .. nplain-1 need no masking: both tiles in the chunk and every position visible
-  // to every row of this wave (tile 2j + 1 ends at (t_begin + 2j + 2) * 32 - 1 <= lim_min).
-  int nplain;
-  {
-    const int jv = ((lim_min + 1) >> 5) - t_begin - 2;  // 2j <= jv
-    nplain = __builtin_amdgcn_readfirstlane(min(jv < 0 ? 0 : jv / 2 + 1, ntiles / 2));
-  }
   const int P = p.page_size;
   const int tpp = P / kTile;  // tiles per page
   // page-table entry of the chunk's last tile
@@ -504,6 +489,31 @@ void decode_kernel(const DecodeParams p) {
     issue_tile(ra, slot_of(st), std::integral_constant<int, 0>{});
     issue_tile(rb, slot_of(st), std::integral_constant<int, 1>{});
   };
+
+  // The first pass's steps 0 and 1 go out now, before the rest of the set-up: they are the
+  // first KV the workgroup waits for, one HBM round trip away.
+  const StepPages sp0 = next_pages();
+  const StepPages sp1 = next_pages();
+  issue_step(0, sp0);
+  issue_step(1, sp1);
+
+  const int wrow0 = row0 + wave * 32;
+  const int R = wrow0 + n;  // this lane's query row (score, P and O layout)
+  const bool row_ok = R < M;
+  // last visible position of the row (bottom-right causal); rows past M are never stored
+  // (computed for every lane, then selected: a branch here would make the compiler spill
+  // around it and wait for the Q DMA)
+  const int lim_r = L - p.q_tokens + (int)fast_div((uint32_t)R, p.div_heads);
+  const int lim = row_ok ? lim_r : 0x7FFFFFFF;
+  const int lim_min = L - p.q_tokens + (int)fast_div((uint32_t)wrow0, p.div_heads);
+  const int nsteps = (ntiles + 1) / 2;
+  // Steps 0 .. nplain-1 need no masking: both tiles in the chunk and every position visible
+  // to every row of this wave (tile 2j + 1 ends at (t_begin + 2j + 2) * 32 - 1 <= lim_min).
+  int nplain;
+  {
+    const int jv = ((lim_min + 1) >> 5) - t_begin - 2;  // 2j <= jv
+    nplain = __builtin_amdgcn_readfirstlane(min(jv < 0 ? 0 : jv / 2 + 1, ntiles / 2));
+  }
 
   const int G16 = lane >> 4, i16 = lane & 15;
   const uint32_t vcol = 16 * (G16 & 1) + 8 * (i16 & 1);
@@ -782,17 +792,18 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll 1
   for (int pass = 0; pass < 2; ++pass) {
     rs.l_run = 0.f;
-    cur_pe = pe_first;
-    cur_po = t_begin - cur_pe * tpp;
-
-    // ---- the query rows (staged above for the first pass; again for a second pass, since
-    // the Q fragments are live within a pass only) with steps 0 and 1 in flight beside them
-    const StepPages sp0 = next_pages();
-    const StepPages sp1 = next_pages();
+    // ---- the query rows and steps 0 and 1 (issued above for the first pass; again for a
+    // second pass, since the Q fragments are live within a pass only), the same order
+    if (pass > 0) {
+      cur_pe = pe_first;
+      cur_po = t_begin - cur_pe * tpp;
+      stage_q();
+      const StepPages spa = next_pages();
+      const StepPages spb = next_pages();
+      issue_step(0, spa);
+      issue_step(1, spb);
+    }
     sp_next = next_pages();  // step 2, issued by stage 0
-    if (pass > 0) stage_q();
-    issue_step(0, sp0);
-    issue_step(1, sp1);
 #pragma unroll
     for (int d = 0; d < 16; ++d) o[d] = (f32x16){0.f};  // while the DMAs are in flight
     wait_vmcnt<2 * kLmin>();  // this wave's Q chunks have landed

@@ -72,6 +72,12 @@ SMALL = [
     ("rows_128", 1, 128, 1, [4500], 0, False, 8, 128),
     ("h256_rows64", 2, 256, 1, [700, 1300], 64, True, 3, 128),
     ("more_splits_than_tiles", 1, 16, 1, [100], 0, False, 16, 128),
+    # pages of an odd number of 32-token tiles (steps straddle pages) and of several pairs
+    ("paged_p96_odd_tiles", 2, 32, 1, [300, 1000], 96, True, 3, 128),
+    ("paged_p128_causal", 2, 16, 4, [130, 1500], 128, True, 4, 128),
+    # a chunk that is a single step, and chunks whose last step has one tile
+    ("one_step_chunks", 1, 16, 1, [64 * 5], 0, False, 5, 128),
+    ("odd_tile_tails", 2, 16, 1, [32 * 7, 32 * 9 + 5], 64, True, 2, 128),
 ]
 
 

@@ -11,6 +11,7 @@
 //
 // HBM-bound: 4 B read + 1 B written per element.  Each thread converts 16 consecutive
 // elements per iteration (four 16-B loads, one 16-B store); the grid strides over the array.
+// Tensors under 2^21 elements (one step's Q) take four elements per thread instead.
 #include "internal.h"
 
 namespace mla {
@@ -43,6 +44,7 @@ __device__ __forceinline__ uint8_t encode1(float t) {
 // Workgroups of kThreads threads; stride = grid * kThreads comes in as an argument, so the
 // kernel reads nothing but its arguments (all fetched in one batch) before its first load.
 constexpr int kThreads = 256;
+constexpr int64_t kSmallN = int64_t(1) << 21;  // below this, four elements per thread
 
 __global__ __launch_bounds__(kThreads) void quantize_vec16(const float4* __restrict__ src,
                                                            uint4* __restrict__ dst, int64_t n16,
@@ -63,7 +65,21 @@ __global__ __launch_bounds__(kThreads) void quantize_vec16(const float4* __restr
   }
 }
 
-// Element-wise variant for unaligned buffers and for the tail after the 16-element blocks.
+// Four elements per thread (one 16-byte load, one 4-byte store): for small tensors such as
+// one step's Q, where spreading the divisions over more threads shortens the kernel (it is
+// latency-bound there, not bandwidth-bound).
+__global__ __launch_bounds__(kThreads) void quantize_vec4(const float4* __restrict__ src,
+                                                          uint32_t* __restrict__ dst, int64_t n4,
+                                                          int64_t stride, float scale) {
+  asm volatile("" ::"s"(src), "s"(dst), "s"(n4), "s"(stride), "s"(scale));
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+    const float4 a = src[i];
+    dst[i] = encode4(__fdiv_rn(a.x, scale), __fdiv_rn(a.y, scale), __fdiv_rn(a.z, scale),
+                     __fdiv_rn(a.w, scale));
+  }
+}
+
+// Element-wise variant for unaligned buffers and for the tail after the vector blocks.
 __global__ __launch_bounds__(kThreads) void quantize_scalar(const float* __restrict__ src,
                                                             uint8_t* __restrict__ dst,
                                                             int64_t begin, int64_t n,
@@ -79,7 +95,13 @@ hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scal
                            hipStream_t s) {
   const bool aligned = ((uintptr_t)src % 16 == 0) && ((uintptr_t)dst % 16 == 0);
   int64_t done = 0;
-  if (aligned && n >= 16) {
+  if ((uintptr_t)src % 16 == 0 && (uintptr_t)dst % 4 == 0 && n >= 4 && n < kSmallN) {
+    const int64_t n4 = n / 4;
+    const int grid = (int)((n4 + kThreads - 1) / kThreads);
+    quantize_vec4<<<grid, kThreads, 0, s>>>((const float4*)src, (uint32_t*)dst, n4,
+                                            (int64_t)grid * kThreads, scale);
+    done = n4 * 4;
+  } else if (aligned && n >= 16) {
     const int64_t n16 = n / 16;
     const int64_t want = (n16 + kThreads - 1) / kThreads;
     const int grid = (int)(want < 8192 ? want : 8192);

@@ -37,6 +37,15 @@ def test_unaligned_and_ragged_buffers():
         got = out.cpu().numpy()
         assert np.array_equal(got[1:1 + hi - lo], ref[lo:hi]), (lo, hi)
         assert got[0] == 0xAA and np.all(got[1 + hi - lo:] == 0xAA)   # nothing written outside
+    # destination 4-byte but not 16-byte aligned, small and large, with ragged tails: the
+    # four-per-thread path, its scalar tail, and the 16-per-thread path
+    for lo, hi in [(0, 4 * 1000 + 3), (4, 4 + 4 * 5000), (0, 1_000_037), (16, (1 << 21) + 16 + 7)]:
+        hi = min(hi, x.size)
+        out = torch.full((hi - lo + 8,), 0xAA, dtype=torch.uint8, device="cuda")
+        mla.quantize_fp8_sat(t[lo:hi], float(s), out=out[4:4 + hi - lo])
+        got = out.cpu().numpy()
+        assert np.array_equal(got[4:4 + hi - lo], ref[lo:hi]), (lo, hi)
+        assert np.all(got[:4] == 0xAA) and np.all(got[4 + hi - lo:] == 0xAA)
 
 
 def _range_hash_oracle(args):

@@ -31,6 +31,14 @@ Pinning (what each function is checked against, in ``tests/test_oracle_*``):
                          causal mask; paged == contiguous; head independence.
 * ``split_partials_fp64`` / ``combine_fp64``  S = 1 identity, the two-split
                          closed form, and split-count independence.
+* ``bf16_bits_to_f32``   torch's bfloat16 -> float32 conversion on all 65536
+                         patterns, and spot values.
+* ``dynamic_quantize``   the scale maps the tensor's largest magnitude to the code
+                         0x7E exactly; bf16 and fp32 sources of the same values agree.
+* ``append_kv_fp8``      appending a request's rows one step at a time and reading
+                         them back through the attention's own gather gives the
+                         quantised rows in order; bytes outside the new rows never
+                         change; one T-row append equals T one-row appends.
 
 No function here is "parity unpinned".
 """
@@ -41,6 +49,7 @@ from .e4m3 import (  # noqa: F401
     per_tensor_scale,
     quantize_e4m3_sat,
 )
+from .cache import append_kv_fp8, bf16_bits_to_f32, dynamic_quantize  # noqa: F401
 from .attention import (  # noqa: F401
     attention_fp64,
     combine_fp64,

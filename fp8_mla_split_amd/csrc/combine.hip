@@ -108,11 +108,15 @@ __device__ __forceinline__ Partial merge_entries(const Partial* red, int nw, int
 template <int kBatch>
 __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
     const uint16_t* __restrict__ po, const float* __restrict__ pl, int S, int R, int nw,
-    float v_scale, uint16_t* __restrict__ out, float* __restrict__ out_lse) {
+    float v_scale, const float* __restrict__ v_scale_dev, uint16_t* __restrict__ out,
+    float* __restrict__ out_lse) {
   static_assert(kCw == 2, "the two split rows of a load sit in lanes l and l + 32");
   // all arguments in one batch of scalar loads (one trip to the argument memory)
   asm volatile("" ::"s"(po), "s"(pl), "s"(S), "s"(R), "s"(nw), "s"(v_scale), "s"(out),
-               "s"(out_lse));
+               "s"(out_lse), "s"(v_scale_dev));
+  // a scale kept on the device (written by an earlier kernel on the stream) replaces v_scale
+  if (v_scale_dev != nullptr)
+    v_scale = *(const __attribute__((address_space(4))) float*)v_scale_dev;
   extern __shared__ Partial red[];  // one entry per (wave, column group)
   const int row = blockIdx.x / kCw;  // b * R + r
   const int chunk = blockIdx.x - row * kCw;
@@ -199,26 +203,29 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
 
 template <int kBatch>
 static void launch_batch(const uint16_t* po, const float* pl, int batch, int splits, int rows,
-                         float v_scale, uint16_t* out, float* out_lse, hipStream_t s) {
+                         float v_scale, const float* v_scale_dev, uint16_t* out, float* out_lse,
+                         hipStream_t s) {
   const int64_t blocks = (int64_t)batch * rows * kCw;
   int nw = (splits + kBatch * kCw - 1) / (kBatch * kCw);
   nw = nw < 1 ? 1 : (nw > kMaxWaves ? kMaxWaves : nw);
   const size_t lds = sizeof(Partial) * kLanesPerRow * nw;
   combine_kernel<kBatch><<<(unsigned)blocks, 64 * nw, lds, s>>>(po, pl, splits, rows, nw,
-                                                                 v_scale, out, out_lse);
+                                                                 v_scale, v_scale_dev, out,
+                                                                 out_lse);
 }
 
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
-                          float v_scale, uint16_t* out, float* out_lse, hipStream_t s) {
+                          float v_scale, const float* v_scale_dev, uint16_t* out, float* out_lse,
+                          hipStream_t s) {
   // As many loads in flight per wave as there are splits to cover, up to 16; from 64 splits
   // on, 8 per wave and twice the waves (up to 16) spread the loads wider (measured on MI355X:
   // 6.2 instead of 6.5 us at 256 splits, 3.9 instead of 4.4 at 64).
   if (splits <= 4 * kCw)
-    launch_batch<4>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
+    launch_batch<4>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, s);
   else if (splits <= 8 * kCw || splits >= 64)
-    launch_batch<8>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
+    launch_batch<8>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, s);
   else
-    launch_batch<16>(po, pl, batch, splits, rows, v_scale, out, out_lse, s);
+    launch_batch<16>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, s);
   return hipGetLastError();
 }
 

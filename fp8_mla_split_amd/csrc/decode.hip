@@ -277,7 +277,7 @@ struct KPair {
   i32x4 a0, a1, b0, b1;
 };
 
-template <bool kPairPages>
+template <bool kPairPages, bool kDevScale>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
@@ -339,6 +339,13 @@ void decode_kernel(const DecodeParams p) {
                                           p.max_pages - 1)];
   int L = seq_lens[b];
   asm volatile("" ::"s"(L), "s"(pt_hint));  // both loads go out before either is waited for
+  // scales kept on the device (written by an earlier kernel on the stream): loaded here, used
+  // first by the softmax of step 0, long after they land
+  float qs_dev = 0.f, ks_dev = 0.f;
+  if constexpr (kDevScale) {
+    qs_dev = *(const __attribute__((address_space(4))) float*)p.q_scale_dev;
+    ks_dev = *(const __attribute__((address_space(4))) float*)p.kv_scale_dev;
+  }
   const int Lmax = p.max_pages * p.page_size;
   L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
   const int ntiles_all = (L + kTile - 1) / kTile;
@@ -520,7 +527,7 @@ void decode_kernel(const DecodeParams p) {
   const uint32_t vrow0 = perm_row(tok_of(gg, i16 >> 1)) * kPitch + vcol;
   const uint32_t vrow1 = perm_row(tok_of(gg, 8 + (i16 >> 1))) * kPitch + vcol;
   const uint32_t krow = perm_row(n) * kPitch + 32 * gg;
-  const float c2 = p.c2;
+  const float c2 = kDevScale ? score_scale_log2(qs_dev, ks_dev, p.softmax_scale) : p.c2;
 
   auto step_base = [&](int st) __attribute__((always_inline)) -> uint32_t {
     return (uint32_t)((st % kStepSlots) * 2 * kSlot);
@@ -909,10 +916,16 @@ hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t 
   const int64_t units = (int64_t)p.batch * p.num_splits;
   const int64_t blocks = ((units + 7) / 8) * 8 * p.groups;
   // an even number of tiles per page (and pages under 4 GiB) takes the paired-tile cursor
-  if ((p.page_size / kTile) % 2 == 0 && p.page_bytes < (int64_t(1) << 32))
-    decode_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(p);
+  const bool paired = (p.page_size / kTile) % 2 == 0 && p.page_bytes < (int64_t(1) << 32);
+  const bool dev = p.q_scale_dev != nullptr;
+  if (paired && !dev)
+    decode_kernel<true, false><<<(unsigned)blocks, 256, 0, s>>>(p);
+  else if (!dev)
+    decode_kernel<false, false><<<(unsigned)blocks, 256, 0, s>>>(p);
+  else if (paired)
+    decode_kernel<true, true><<<(unsigned)blocks, 256, 0, s>>>(p);
   else
-    decode_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(p);
+    decode_kernel<false, true><<<(unsigned)blocks, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

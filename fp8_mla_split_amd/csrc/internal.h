@@ -49,14 +49,32 @@ struct DecodeParams {
   FastDiv div_splits, div_groups, div_heads, div_tpp;  // by num_splits, groups, heads, page_size/32
   float c2;                           // q_scale * kv_scale * softmax_scale * log2(e)
   float kv_scale;
+  // scales read on the device instead (q_scale_dev[0], kv_scale_dev[0]); c2 is then formed in
+  // the kernel with the same double-precision products the host uses
+  const float* q_scale_dev;
+  const float* kv_scale_dev;
+  float softmax_scale;
 };
 
+// c2 from the three scales: products in double, one rounding to float (host and device alike)
+__host__ __device__ inline float score_scale_log2(float q_scale, float kv_scale, float sm_scale) {
+  return (float)((double)q_scale * kv_scale * sm_scale * 1.4426950408889634);
+}
+
 hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scale, hipStream_t s);
+int64_t dynamic_quantize_workspace_bytes();
+hipError_t launch_quantize_dynamic(const void* src, bool bf16, uint8_t* dst, int64_t n,
+                                   float* scale_out, void* workspace, hipStream_t s);
+hipError_t launch_kv_append(const float* src, uint8_t* pool, int64_t num_pages,
+                            const int32_t* page_table, const int32_t* seq_lens, int batch,
+                            int t_new, int page_size, int max_pages, float scale, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t s);
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int grid,
                              hipStream_t s);
 int64_t read_probe_chunk_bytes();
+// v_scale_dev: NULL, or a device float that replaces v_scale
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
-                          float v_scale, uint16_t* out, float* out_lse, hipStream_t s);
+                          float v_scale, const float* v_scale_dev, uint16_t* out, float* out_lse,
+                          hipStream_t s);
 
 }  // namespace mla

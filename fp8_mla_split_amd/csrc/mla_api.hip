@@ -97,6 +97,41 @@ mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t 
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+mla_status mla_quantize_fp8_sat_dynamic(const void* src_dev, int src_dtype, uint8_t* dst_dev,
+                                        int64_t n, float* scale_dev, void* workspace_dev,
+                                        int64_t workspace_bytes, void* stream) {
+  if (n < 0 || (src_dtype != MLA_SRC_F32 && src_dtype != MLA_SRC_BF16)) return MLA_ERR_INVALID_ARG;
+  if (n == 0) return MLA_OK;
+  if (!src_dev || !dst_dev || !scale_dev || !workspace_dev) return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)workspace_dev & 3) != 0 || ((uintptr_t)scale_dev & 3) != 0 ||
+      ((uintptr_t)src_dev & (src_dtype == MLA_SRC_BF16 ? 1 : 3)) != 0)
+    return MLA_ERR_INVALID_ARG;
+  if (workspace_bytes < mla::dynamic_quantize_workspace_bytes()) return MLA_ERR_WORKSPACE;
+  const hipError_t e = mla::launch_quantize_dynamic(src_dev, src_dtype == MLA_SRC_BF16, dst_dev,
+                                                    n, scale_dev, workspace_dev,
+                                                    (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_kv_append_fp8_sat(const float* new_kv_dev, uint8_t* kv_pool_dev, int64_t num_pages,
+                                 const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                                 int batch, int new_tokens, int page_size, int max_pages,
+                                 float kv_scale, void* stream) {
+  if (batch < 0 || new_tokens < 0 || page_size < 1 || max_pages < 1 || num_pages < 1 ||
+      !good_scale(kv_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (batch == 0 || new_tokens == 0) return MLA_OK;
+  if (!new_kv_dev || !kv_pool_dev || !page_table_dev || !seq_lens_dev) return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)new_kv_dev & 3) != 0) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)batch * new_tokens > 0x7FFFFFFFLL ||
+      (int64_t)max_pages * page_size > 0x7FFFFFFFLL)
+    return MLA_ERR_UNSUPPORTED;
+  const hipError_t e = mla::launch_kv_append(new_kv_dev, kv_pool_dev, num_pages, page_table_dev,
+                                             seq_lens_dev, batch, new_tokens, page_size,
+                                             max_pages, kv_scale, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
                             int64_t total_kv_tokens, int cu_count, int* num_splits,
                             int* rows_per_group, int64_t* partial_rows) {
@@ -117,21 +152,30 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
   return MLA_OK;
 }
 
-mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
-                              const int32_t* page_table_dev, const int32_t* seq_lens_dev,
-                              int batch, int q_tokens, int heads, int page_size, int max_pages,
-                              int max_seq_len, float q_scale, float kv_scale, float softmax_scale,
-                              int num_splits, int rows_per_group, uint16_t* partial_o_dev,
-                              float* partial_lse_dev, int64_t partial_rows_capacity,
-                              void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points: host scales (q_dev == kv_dev == NULL) or device scales.
+mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                         const int32_t* page_table_dev, const int32_t* seq_lens_dev, int batch,
+                         int q_tokens, int heads, int page_size, int max_pages, int max_seq_len,
+                         float q_scale, float kv_scale, const float* q_scale_dev,
+                         const float* kv_scale_dev, float softmax_scale, int num_splits,
+                         int rows_per_group, uint16_t* partial_o_dev, float* partial_lse_dev,
+                         int64_t partial_rows_capacity, void* stream) {
+  const bool dev = q_scale_dev != nullptr;
   if (batch < 0 || q_tokens < 1 || heads < 1 || page_size < 1 || max_pages < 1 ||
       num_splits < 0 || rows_per_group < 0 || partial_rows_capacity < 0)
     return MLA_ERR_INVALID_ARG;
-  if (!good_scale(q_scale) || !good_scale(kv_scale) || !good_scale(softmax_scale))
+  if ((!dev && (!good_scale(q_scale) || !good_scale(kv_scale))) || !good_scale(softmax_scale))
     return MLA_ERR_INVALID_ARG;
   if (batch == 0) return MLA_OK;
   if (!q8_dev || !kv_pool_dev || !page_table_dev || !seq_lens_dev || !partial_o_dev ||
       !partial_lse_dev)
+    return MLA_ERR_INVALID_ARG;
+  if (dev && (kv_scale_dev == nullptr || ((uintptr_t)q_scale_dev & 3) != 0 ||
+              ((uintptr_t)kv_scale_dev & 3) != 0))
     return MLA_ERR_INVALID_ARG;
   const int64_t M = (int64_t)q_tokens * heads;
   if (M > mla::kMaxRows || page_size % mla::kTile != 0 ||
@@ -180,26 +224,81 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   p.div_groups = mla::make_fastdiv((uint32_t)groups);
   p.div_heads = mla::make_fastdiv((uint32_t)heads);
   p.div_tpp = mla::make_fastdiv((uint32_t)(page_size / mla::kTile));
-  p.c2 = (float)((double)q_scale * kv_scale * softmax_scale * 1.4426950408889634);
+  p.c2 = dev ? 0.f : mla::score_scale_log2(q_scale, kv_scale, softmax_scale);
   p.kv_scale = kv_scale;
+  p.q_scale_dev = q_scale_dev;
+  p.kv_scale_dev = kv_scale_dev;
+  p.softmax_scale = softmax_scale;
   const hipError_t e = mla::launch_decode(p, r, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status combine_common(const uint16_t* partial_o_dev, const float* partial_lse_dev,
+                          int batch, int num_splits, int q_tokens, int heads, float v_scale,
+                          const float* v_scale_dev, uint16_t* out_bf16_dev, float* out_lse_dev,
+                          void* stream) {
+  if (batch < 0 || num_splits < 1 || q_tokens < 1 || heads < 1) return MLA_ERR_INVALID_ARG;
+  if (v_scale_dev == nullptr && !good_scale(v_scale)) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!partial_o_dev || !partial_lse_dev || !out_bf16_dev) return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)v_scale_dev & 3) != 0) return MLA_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)q_tokens * heads;
+  if (M > mla::kMaxRows || num_splits > mla::kMaxSplitsCombine) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * M * 2 > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+  const hipError_t e = mla::launch_combine(partial_o_dev, partial_lse_dev, batch, num_splits,
+                                           (int)M, v_scale, v_scale_dev, out_bf16_dev,
+                                           out_lse_dev, (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                              const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                              int batch, int q_tokens, int heads, int page_size, int max_pages,
+                              int max_seq_len, float q_scale, float kv_scale, float softmax_scale,
+                              int num_splits, int rows_per_group, uint16_t* partial_o_dev,
+                              float* partial_lse_dev, int64_t partial_rows_capacity,
+                              void* stream) {
+  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, batch, q_tokens, heads,
+                       page_size, max_pages, max_seq_len, q_scale, kv_scale, nullptr, nullptr,
+                       softmax_scale, num_splits, rows_per_group, partial_o_dev, partial_lse_dev,
+                       partial_rows_capacity, stream);
+}
+
+mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                                         const int32_t* page_table_dev,
+                                         const int32_t* seq_lens_dev, int batch, int q_tokens,
+                                         int heads, int page_size, int max_pages,
+                                         int max_seq_len, const float* q_scale_dev,
+                                         const float* kv_scale_dev, float softmax_scale,
+                                         int num_splits, int rows_per_group,
+                                         uint16_t* partial_o_dev, float* partial_lse_dev,
+                                         int64_t partial_rows_capacity, void* stream) {
+  if (q_scale_dev == nullptr || kv_scale_dev == nullptr) return MLA_ERR_INVALID_ARG;
+  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, batch, q_tokens, heads,
+                       page_size, max_pages, max_seq_len, 1.0f, 1.0f, q_scale_dev, kv_scale_dev,
+                       softmax_scale, num_splits, rows_per_group, partial_o_dev, partial_lse_dev,
+                       partial_rows_capacity, stream);
 }
 
 mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* partial_lse_dev,
                                int batch, int num_splits, int q_tokens, int heads, float v_scale,
                                uint16_t* out_bf16_dev, float* out_lse_dev, void* stream) {
-  if (batch < 0 || num_splits < 1 || q_tokens < 1 || heads < 1) return MLA_ERR_INVALID_ARG;
-  if (!good_scale(v_scale)) return MLA_ERR_INVALID_ARG;
-  if (batch == 0) return MLA_OK;
-  if (!partial_o_dev || !partial_lse_dev || !out_bf16_dev) return MLA_ERR_INVALID_ARG;
-  const int64_t M = (int64_t)q_tokens * heads;
-  if (M > mla::kMaxRows || num_splits > mla::kMaxSplitsCombine) return MLA_ERR_UNSUPPORTED;
-  if ((int64_t)batch * M * 2 > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
-  const hipError_t e = mla::launch_combine(partial_o_dev, partial_lse_dev, batch, num_splits,
-                                           (int)M, v_scale, out_bf16_dev, out_lse_dev,
-                                           (hipStream_t)stream);
-  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return combine_common(partial_o_dev, partial_lse_dev, batch, num_splits, q_tokens, heads,
+                        v_scale, nullptr, out_bf16_dev, out_lse_dev, stream);
+}
+
+mla_status mla_splitkv_combine_dev_scale(const uint16_t* partial_o_dev,
+                                         const float* partial_lse_dev, int batch,
+                                         int num_splits, int q_tokens, int heads,
+                                         const float* v_scale_dev, uint16_t* out_bf16_dev,
+                                         float* out_lse_dev, void* stream) {
+  if (v_scale_dev == nullptr) return MLA_ERR_INVALID_ARG;
+  return combine_common(partial_o_dev, partial_lse_dev, batch, num_splits, q_tokens, heads, 1.0f,
+                        v_scale_dev, out_bf16_dev, out_lse_dev, stream);
 }
 
 mla_status mla_hbm_read_probe(const void* buf_dev, int64_t bytes, uint32_t* out_dev,

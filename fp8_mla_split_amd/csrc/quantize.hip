@@ -89,7 +89,234 @@ __global__ __launch_bounds__(kThreads) void quantize_scalar(const float* __restr
     dst[i] = encode1(__fdiv_rn(src[i], scale));
 }
 
+// ---- Appending a decode step's new KV rows to the paged FP8 cache ----------------------
+// New token t of request b (of T) is logical position n = seq_lens[b] - T + t and goes to row
+// n % P of page page_table[b, n / P].  One thread per 16 columns of a 576-wide row (36 per
+// row: four 16-B fp32 loads, one 16-B store), or per column where a buffer is not 16-byte
+// aligned.  Positions past the page table and page ids outside the pool are skipped, so a
+// bad device-side length or table entry cannot write outside the pool.
+template <bool Vec>
+__global__ __launch_bounds__(kThreads) void kv_append(const float* __restrict__ src,
+                                                      uint8_t* __restrict__ pool,
+                                                      const int32_t* __restrict__ page_table,
+                                                      const int32_t* __restrict__ seq_lens,
+                                                      int t_new, int page_size, int max_pages,
+                                                      int64_t num_pages, int64_t units,
+                                                      int64_t stride, float scale) {
+  constexpr int kPer = Vec ? 16 : 1;
+  constexpr int kUnitsPerRow = kD / kPer;
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
+    const int64_t row = u / kUnitsPerRow;
+    const int c = (int)(u - row * kUnitsPerRow);
+    const int b = (int)(row / t_new), t = (int)(row - (int64_t)b * t_new);
+    const int64_t n = (int64_t)seq_lens[b] - t_new + t;
+    if (n < 0 || n >= (int64_t)max_pages * page_size) continue;
+    const int64_t page = page_table[(int64_t)b * max_pages + n / page_size];
+    if (page < 0 || page >= num_pages) continue;
+    uint8_t* d = pool + (page * page_size + n % page_size) * kD + c * kPer;
+    const float* x = src + row * kD + c * kPer;
+    if constexpr (Vec) {
+      const float4* x4 = (const float4*)x;
+      const float4 a = x4[0], bb = x4[1], cc = x4[2], dd = x4[3];
+      uint4 o;
+      o.x = encode4(__fdiv_rn(a.x, scale), __fdiv_rn(a.y, scale), __fdiv_rn(a.z, scale),
+                    __fdiv_rn(a.w, scale));
+      o.y = encode4(__fdiv_rn(bb.x, scale), __fdiv_rn(bb.y, scale), __fdiv_rn(bb.z, scale),
+                    __fdiv_rn(bb.w, scale));
+      o.z = encode4(__fdiv_rn(cc.x, scale), __fdiv_rn(cc.y, scale), __fdiv_rn(cc.z, scale),
+                    __fdiv_rn(cc.w, scale));
+      o.w = encode4(__fdiv_rn(dd.x, scale), __fdiv_rn(dd.y, scale), __fdiv_rn(dd.z, scale),
+                    __fdiv_rn(dd.w, scale));
+      *(uint4*)d = o;
+    } else {
+      *d = encode1(__fdiv_rn(*x, scale));
+    }
+  }
+}
+
+// ---- Per-tensor scale taken from the data (amax / 448), then the same encode ----------
+// Pass 1 writes one maximum per workgroup; pass 2 has every workgroup fold those maxima
+// (at most kAmaxBlocks words, from L2), derive the scale and quantise its share.  No atomics
+// and nothing to clear beforehand, so both passes can be replayed in a captured graph.
+// Magnitudes are compared as the bit patterns of |x| (sign cleared): for non-negative IEEE
+// values the unsigned order is the numeric order, and every NaN pattern sorts above +inf,
+// so the result is NaN whenever the tensor holds one, as max|x| is.
+constexpr int kAmaxBlocks = 1024;
+
+// bf16 sources hold the upper halves of fp32 patterns.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t abs_bits_word(uint32_t w, bool bf16) {
+  return bf16 ? umax(w & 0x7FFF0000u, (w & 0x7FFFu) << 16) : (w & 0x7FFFFFFFu);
+}
+
+__device__ __forceinline__ uint32_t abs_bits_16b(const uint4& v, bool bf16) {
+  return umax(umax(abs_bits_word(v.x, bf16), abs_bits_word(v.y, bf16)),
+              umax(abs_bits_word(v.z, bf16), abs_bits_word(v.w, bf16)));
+}
+
+__device__ __forceinline__ float load_elem(const void* src, int64_t i, bool bf16) {
+  return bf16 ? __uint_as_float((uint32_t)((const uint16_t*)src)[i] << 16)
+              : ((const float*)src)[i];
+}
+
+// Largest value of a workgroup (all threads return it).
+__device__ __forceinline__ uint32_t block_umax(uint32_t m) {
+  __shared__ uint32_t red[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = umax(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = umax(m, red[w]);
+  return m;
+}
+
+// src: 16-byte aligned when vec (16-B words = 4 fp32 or 8 bf16 values, four words in flight
+// per thread); the elements after the last whole word are read one at a time.
+template <bool Bf16>
+__global__ __launch_bounds__(kThreads) void amax_partial(const void* __restrict__ src,
+                                                         int64_t n, int vec,
+                                                         uint32_t* __restrict__ partial) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t m = 0;
+  int64_t done = 0;
+  if (vec) {
+    constexpr int kPerWord = Bf16 ? 8 : 4;
+    const int64_t nw = n / kPerWord;
+    const uint4* w = (const uint4*)src;
+    int64_t i = tid;
+    for (; i + 3 * stride < nw; i += 4 * stride) {
+      const uint4 a = w[i], b = w[i + stride], c = w[i + 2 * stride], d = w[i + 3 * stride];
+      m = umax(m, umax(umax(abs_bits_16b(a, Bf16), abs_bits_16b(b, Bf16)),
+                       umax(abs_bits_16b(c, Bf16), abs_bits_16b(d, Bf16))));
+    }
+    for (; i < nw; i += stride) m = umax(m, abs_bits_16b(w[i], Bf16));
+    done = nw * kPerWord;
+  }
+  for (int64_t i = done + tid; i < n; i += stride)
+    m = umax(m, __float_as_uint(load_elem(src, i, Bf16)) & 0x7FFFFFFFu);
+  m = block_umax(m);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// Pass 2.  Per = elements per thread and iteration: 16 (16-B stores), 4 (4-B stores; small
+// tensors, where more threads shorten the latency-bound kernel) or 1 (unaligned buffers).
+template <bool Bf16, int Per>
+__global__ __launch_bounds__(kThreads) void quantize_from_amax(
+    const void* __restrict__ src, uint8_t* __restrict__ dst, int64_t n, int64_t stride,
+    const uint32_t* __restrict__ partial, int nparts, float* __restrict__ scale_out) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) m = umax(m, partial[i]);
+  const float amax = __uint_as_float(block_umax(m));
+  const float scale = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale_out = scale;
+  const int64_t groups = n / Per;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups; g += stride) {
+    float x[Per];
+    if constexpr (Per == 1) {
+      x[0] = load_elem(src, g, Bf16);
+    } else if constexpr (Bf16) {
+      uint32_t w[Per / 2];
+      if constexpr (Per == 16) {
+        const uint4 a = ((const uint4*)src)[2 * g], b = ((const uint4*)src)[2 * g + 1];
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+      } else {
+        const uint2 a = ((const uint2*)src)[g];
+        w[0] = a.x; w[1] = a.y;
+      }
+#pragma unroll
+      for (int k = 0; k < Per / 2; ++k) {
+        x[2 * k] = bf16_lo(w[k]);
+        x[2 * k + 1] = bf16_hi(w[k]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < Per / 4; ++k) {
+        const float4 a = ((const float4*)src)[(Per / 4) * g + k];
+        x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
+      }
+    }
+    if constexpr (Per == 1) {
+      dst[g] = encode1(__fdiv_rn(x[0], scale));
+    } else {
+      uint32_t o[Per / 4];
+#pragma unroll
+      for (int k = 0; k < Per / 4; ++k)
+        o[k] = encode4(__fdiv_rn(x[4 * k], scale), __fdiv_rn(x[4 * k + 1], scale),
+                       __fdiv_rn(x[4 * k + 2], scale), __fdiv_rn(x[4 * k + 3], scale));
+      if constexpr (Per == 16)
+        ((uint4*)dst)[g] = make_uint4(o[0], o[1], o[2], o[3]);
+      else
+        ((uint32_t*)dst)[g] = o[0];
+    }
+  }
+  // elements after the last whole group
+  if (blockIdx.x == 0)
+    for (int64_t i = groups * Per + threadIdx.x; i < n; i += kThreads)
+      dst[i] = encode1(__fdiv_rn(load_elem(src, i, Bf16), scale));
+}
+
+int grid_for(int64_t units, int64_t cap) {
+  const int64_t want = (units + kThreads - 1) / kThreads;
+  return (int)(want < 1 ? 1 : (want < cap ? want : cap));
+}
+
+template <bool Bf16>
+hipError_t launch_dynamic_t(const void* src, uint8_t* dst, int64_t n, float* scale_out,
+                            uint32_t* partial, hipStream_t s) {
+  const int esz = Bf16 ? 2 : 4;
+  const bool src16 = (uintptr_t)src % 16 == 0;
+  const int64_t words = src16 ? n * esz / 16 : n;
+  const int ablocks = grid_for((words + 3) / 4, kAmaxBlocks);
+  amax_partial<Bf16><<<ablocks, kThreads, 0, s>>>(src, n, src16 ? 1 : 0, partial);
+  if (src16 && (uintptr_t)dst % 4 == 0 && n < kSmallN) {
+    const int grid = grid_for(n / 4, 8192);
+    quantize_from_amax<Bf16, 4><<<grid, kThreads, 0, s>>>(src, dst, n, (int64_t)grid * kThreads,
+                                                          partial, ablocks, scale_out);
+  } else if (src16 && (uintptr_t)dst % 16 == 0) {
+    const int grid = grid_for(n / 16, 8192);
+    quantize_from_amax<Bf16, 16><<<grid, kThreads, 0, s>>>(src, dst, n, (int64_t)grid * kThreads,
+                                                           partial, ablocks, scale_out);
+  } else {
+    const int grid = grid_for(n, 8192);
+    quantize_from_amax<Bf16, 1><<<grid, kThreads, 0, s>>>(src, dst, n, (int64_t)grid * kThreads,
+                                                          partial, ablocks, scale_out);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int64_t dynamic_quantize_workspace_bytes() { return (int64_t)kAmaxBlocks * 4; }
+
+hipError_t launch_quantize_dynamic(const void* src, bool bf16, uint8_t* dst, int64_t n,
+                                   float* scale_out, void* workspace, hipStream_t s) {
+  return bf16 ? launch_dynamic_t<true>(src, dst, n, scale_out, (uint32_t*)workspace, s)
+              : launch_dynamic_t<false>(src, dst, n, scale_out, (uint32_t*)workspace, s);
+}
+
+hipError_t launch_kv_append(const float* src, uint8_t* pool, int64_t num_pages,
+                            const int32_t* page_table, const int32_t* seq_lens, int batch,
+                            int t_new, int page_size, int max_pages, float scale, hipStream_t s) {
+  const bool vec = (uintptr_t)src % 16 == 0 && (uintptr_t)pool % 16 == 0;
+  const int64_t units = (int64_t)batch * t_new * (vec ? kD / 16 : kD);
+  const int grid = grid_for(units, 8192);
+  const int64_t stride = (int64_t)grid * kThreads;
+  if (vec)
+    kv_append<true><<<grid, kThreads, 0, s>>>(src, pool, page_table, seq_lens, t_new, page_size,
+                                              max_pages, num_pages, units, stride, scale);
+  else
+    kv_append<false><<<grid, kThreads, 0, s>>>(src, pool, page_table, seq_lens, t_new, page_size,
+                                               max_pages, num_pages, units, stride, scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scale,
                            hipStream_t s) {

@@ -33,10 +33,24 @@ _lib.mla_decode_splitkv.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, 
                                     _f32, _f32, _f32, _i32, _i32, _vp, _vp, _i64, _vp]
 _lib.mla_splitkv_combine.restype = _i32
 _lib.mla_splitkv_combine.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp]
+_lib.mla_decode_splitkv_dev_scales.restype = _i32
+_lib.mla_decode_splitkv_dev_scales.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _vp, _vp, _f32, _i32, _i32, _vp, _vp, _i64,
+                                               _vp]
+_lib.mla_splitkv_combine_dev_scale.restype = _i32
+_lib.mla_splitkv_combine_dev_scale.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                               _vp]
+_lib.mla_quantize_fp8_sat_dynamic.restype = _i32
+_lib.mla_quantize_fp8_sat_dynamic.argtypes = [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _vp]
+_lib.mla_kv_append_fp8_sat.restype = _i32
+_lib.mla_kv_append_fp8_sat.argtypes = [_vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
+                                       _vp]
 _lib.mla_hbm_read_probe.restype = _i32
 _lib.mla_hbm_read_probe.argtypes = [_vp, _i64, _vp, _i32, _vp]
 
 D_KV, D_V = 576, 512
+QUANTIZE_DYNAMIC_WORKSPACE_BYTES = 4096  # MLA_QUANTIZE_DYNAMIC_WORKSPACE_BYTES
+_SRC_DTYPE = {torch.float32: 0, torch.bfloat16: 1}  # MLA_SRC_F32, MLA_SRC_BF16
 
 
 class MLAError(RuntimeError):
@@ -87,6 +101,63 @@ def quantize_fp8_sat(x: torch.Tensor, scale: float, out: Optional[torch.Tensor] 
     return out
 
 
+def quantize_fp8_sat_dynamic(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+                             scale: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None):
+    """Per-tensor scale amax / 448 taken on the device, then the saturating encode.
+
+    x: fp32 or bf16 on the GPU.  Returns ``(codes uint8 [x.shape], scale fp32 [1])``; the
+    scale stays on the device (pass it to decode_splitkv / splitkv_combine as is)."""
+    if not x.is_cuda or x.dtype not in _SRC_DTYPE or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 or bf16 tensor on the GPU")
+    dev = x.device
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(QUANTIZE_DYNAMIC_WORKSPACE_BYTES // 4, dtype=torch.int32,
+                                device=dev)
+    _dev_tensor(out, torch.uint8, "out")
+    _dev_tensor(scale, torch.float32, "scale")
+    if out.numel() != x.numel():
+        raise ValueError("out must have as many elements as x")
+    _check(_lib.mla_quantize_fp8_sat_dynamic(
+        _ptr(x), _SRC_DTYPE[x.dtype], _ptr(out), x.numel(), _ptr(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev)),
+        "mla_quantize_fp8_sat_dynamic")
+    return out, scale
+
+
+def kv_append_fp8_sat(new_kv: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.Tensor,
+                      seq_lens: torch.Tensor, kv_scale: float) -> None:
+    """Quantise new_kv [B, T, 576] (fp32) into the paged cache kv_pool8 [pages, P, 576] at
+    positions seq_lens[b] - T + t (seq_lens already counts the new tokens)."""
+    _dev_tensor(new_kv, torch.float32, "new_kv")
+    _dev_tensor(kv_pool8, torch.uint8, "kv_pool8")
+    _dev_tensor(page_table, torch.int32, "page_table")
+    _dev_tensor(seq_lens, torch.int32, "seq_lens")
+    if new_kv.dim() != 3 or new_kv.shape[2] != D_KV or kv_pool8.dim() != 3 or \
+            kv_pool8.shape[2] != D_KV:
+        raise ValueError("new_kv and kv_pool8 rows must be 576 wide")
+    B, T = new_kv.shape[0], new_kv.shape[1]
+    if page_table.dim() != 2 or page_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("page_table must be [B, max_pages] and seq_lens [B]")
+    _check(_lib.mla_kv_append_fp8_sat(
+        _ptr(new_kv), _ptr(kv_pool8), kv_pool8.shape[0], _ptr(page_table), _ptr(seq_lens), B, T,
+        kv_pool8.shape[1], page_table.shape[1], float(kv_scale), _stream(new_kv.device)),
+        "mla_kv_append_fp8_sat")
+
+
+def _dev_scale(t, name: str) -> bool:
+    """True for a device scale (a 1-element fp32 GPU tensor), False for a host number."""
+    if isinstance(t, torch.Tensor):
+        if not t.is_cuda or t.dtype != torch.float32 or t.numel() < 1:
+            raise ValueError(f"{name} as a tensor must be fp32 on the GPU")
+        return True
+    return False
+
+
 def splitkv_plan(batch: int, q_tokens: int, heads: int, max_seq_len: int,
                  cu_count: int = 0, total_kv_tokens: int = 0) -> Plan:
     """Split count and row grouping; total_kv_tokens = the sum of the requests' lengths if
@@ -105,6 +176,8 @@ def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.T
                    rows_per_group: int = 0, partial_o: Optional[torch.Tensor] = None,
                    partial_lse: Optional[torch.Tensor] = None):
     """Split-KV partial attention.  Returns ``(partial_o, partial_lse, num_splits)``.
+    q_scale and kv_scale are host numbers, or both 1-element fp32 device tensors (e.g. from
+    quantize_fp8_sat_dynamic), which selects mla_decode_splitkv_dev_scales.
 
     q8 [B, Sq, H, 576] uint8; kv_pool8 [pages, page_size, 576] uint8; page_table
     [B, max_pages] int32; seq_lens [B] int32.  partial_o [B, S, Sq*H, 512] fp16 (in units of
@@ -131,6 +204,16 @@ def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.T
     _dev_tensor(partial_o, torch.float16, "partial_o")
     _dev_tensor(partial_lse, torch.float32, "partial_lse")
     cap = min(partial_o.numel() // D_V, partial_lse.numel())
+    dq, dk = _dev_scale(q_scale, "q_scale"), _dev_scale(kv_scale, "kv_scale")
+    if dq != dk:
+        raise ValueError("q_scale and kv_scale must both be host numbers or both device tensors")
+    if dq:
+        _check(_lib.mla_decode_splitkv_dev_scales(
+            _ptr(q8), _ptr(kv_pool8), _ptr(page_table), _ptr(seq_lens), B, Sq, H, page_size,
+            page_table.shape[1], max_seq_len, _ptr(q_scale), _ptr(kv_scale),
+            float(softmax_scale), num_splits, rows_per_group, _ptr(partial_o),
+            _ptr(partial_lse), cap, _stream(q8.device)), "mla_decode_splitkv_dev_scales")
+        return partial_o, partial_lse, num_splits
     _check(_lib.mla_decode_splitkv(
         _ptr(q8), _ptr(kv_pool8), _ptr(page_table), _ptr(seq_lens), B, Sq, H, page_size,
         page_table.shape[1], max_seq_len, float(q_scale), float(kv_scale),
@@ -143,7 +226,8 @@ def splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens
                     heads: int, v_scale: float, out: Optional[torch.Tensor] = None,
                     out_lse: Optional[torch.Tensor] = None, want_lse: bool = True):
     """LSE merge -> (out [B, Sq, H, 512] bf16, lse [B, Sq, H] fp32 or None).  partial_o is
-    fp16 in units of v_scale (the KV scale), as decode_splitkv writes it."""
+    fp16 in units of v_scale (the KV scale), as decode_splitkv writes it; v_scale may be a
+    1-element fp32 device tensor (mla_splitkv_combine_dev_scale)."""
     _dev_tensor(partial_o, torch.float16, "partial_o")
     _dev_tensor(partial_lse, torch.float32, "partial_lse")
     B, S = partial_lse.shape[0], partial_lse.shape[1]
@@ -157,6 +241,12 @@ def splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens
     _dev_tensor(out, torch.bfloat16, "out")
     if out_lse is not None:
         _dev_tensor(out_lse, torch.float32, "out_lse")
+    if _dev_scale(v_scale, "v_scale"):
+        _check(_lib.mla_splitkv_combine_dev_scale(_ptr(partial_o), _ptr(partial_lse), B, S,
+                                                  q_tokens, heads, _ptr(v_scale), _ptr(out),
+                                                  _ptr(out_lse), _stream(dev)),
+               "mla_splitkv_combine_dev_scale")
+        return out, out_lse
     _check(_lib.mla_splitkv_combine(_ptr(partial_o), _ptr(partial_lse), B, S, q_tokens, heads,
                                     float(v_scale), _ptr(out), _ptr(out_lse), _stream(dev)),
            "mla_splitkv_combine")

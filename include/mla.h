@@ -70,6 +70,62 @@ mla_status mla_quantize_fp8_sat(const float* src_dev, uint8_t* dst_dev, int64_t 
                                 void* stream);
 
 /*
+ * Saturating FP8 quantisation with the per-tensor scale taken from the data on the device
+ * ([A/MLA] item (4); the scale is the usual amax / 448, so the caller needs no host copy of
+ * the tensor's range and no synchronisation before the decode):
+ *
+ *   x_i       = src_dev[i] as fp32 (a bf16 source is widened exactly: its bits are the upper
+ *               half of the fp32 pattern)
+ *   amax      = max_i |x_i|
+ *   scale     = 1 if amax == 0, else float32(amax) / 448 (IEEE fp32 division)
+ *   dst_dev[i] = the code of mla_quantize_fp8_sat for x_i with that scale
+ *   scale_dev[0] = scale
+ *
+ * A tensor holding a NaN gets a NaN scale (and NaN codes); one holding +-inf an inf scale.
+ *   src_dev   : device, fp32 [n] (src_dtype MLA_SRC_F32, 4-byte aligned) or bf16 bit
+ *               patterns [n] (MLA_SRC_BF16, 2-byte aligned).
+ *   dst_dev   : uint8 [n], device (may not alias src_dev).   n >= 0 (0 enqueues nothing).
+ *   scale_dev : one float, device, 4-byte aligned; written by the second of the two kernels
+ *               this call enqueues (the first writes per-workgroup maxima to the workspace).
+ *   workspace_dev / workspace_bytes : device scratch, 4-byte aligned, at least
+ *               MLA_QUANTIZE_DYNAMIC_WORKSPACE_BYTES; its contents on entry do not matter.
+ *               Calls that share a workspace must not run concurrently.
+ * Errors: INVALID_ARG (n < 0, unknown dtype, NULL or misaligned pointers with n > 0);
+ * WORKSPACE (workspace too small); HIP.
+ */
+#define MLA_QUANTIZE_DYNAMIC_WORKSPACE_BYTES 4096
+enum { MLA_SRC_F32 = 0, MLA_SRC_BF16 = 1 };
+mla_status mla_quantize_fp8_sat_dynamic(const void* src_dev, int src_dtype, uint8_t* dst_dev,
+                                        int64_t n, float* scale_dev, void* workspace_dev,
+                                        int64_t workspace_bytes, void* stream);
+
+/*
+ * Append a decode step's new latent + rope rows to the paged FP8 KV cache, quantised on the
+ * way in ([A/MLA] item (4): KV is converted to FP8 before the attention reads it; here the
+ * conversion writes straight into the cache the decode call reads).
+ *
+ * New token t (0 <= t < T) of request b is logical position n = seq_lens_dev[b] - T + t, i.e.
+ * seq_lens_dev already counts the T new tokens, as mla_decode_splitkv expects.  Its row
+ *   kv_pool[page_table[b, n / page_size], n % page_size, 0:576]
+ *     = e4m3_sat_rne(float32(new_kv[b, t, :]) / kv_scale)      (as mla_quantize_fp8_sat)
+ * Positions outside [0, max_pages * page_size) and page ids outside [0, num_pages) are not
+ * written; no other byte of the pool changes.  If two new rows name the same cache row,
+ * which one lands is unspecified.
+ *   new_kv_dev     fp32 [B, T, 576], device, 4-byte aligned (16-byte alignment of it and of
+ *                  the pool takes the vector path); may not alias the pool.
+ *   kv_pool_dev    uint8 [num_pages, page_size, 576], device.
+ *   page_table_dev int32 [B, max_pages];  seq_lens_dev int32 [B]  (device).
+ *   kv_scale       the cache's dequantisation scale: finite, > 0.
+ * Errors: INVALID_ARG (negative sizes, page_size/max_pages/num_pages < 1, bad scale, NULL or
+ * misaligned pointers with B*T > 0); UNSUPPORTED (B*T or max_pages*page_size >= 2^31); HIP.
+ * B == 0 or T == 0 enqueues nothing.
+ */
+mla_status mla_kv_append_fp8_sat(const float* new_kv_dev, uint8_t* kv_pool_dev, int64_t num_pages,
+                                 const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                                 int batch, int new_tokens, int page_size, int max_pages,
+                                 float kv_scale, void* stream);
+
+/*
  * Split planner ([A/MLA] item (3): at batch 1 a fixed split count leaves most compute units
  * idle; the count has to follow the machine and the shape).  Chooses, from the compute-unit
  * count, the batch, the number of query rows (q_tokens * heads) and the longest context:
@@ -137,6 +193,27 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                               int64_t partial_rows_capacity, void* stream);
 
 /*
+ * mla_decode_splitkv with both dequantisation scales read on the device: q_scale_dev[0] and
+ * kv_scale_dev[0] (4-byte aligned device floats, e.g. written by
+ * mla_quantize_fp8_sat_dynamic earlier on the same stream) take the place of q_scale and
+ * kv_scale, so a step whose Q scale comes from the data needs no host round trip
+ * ([A/MLA] item (4) with a data-derived scale).  The kernel forms the score factor from them
+ * exactly as the host does (products in double, one rounding to float), so equal scale
+ * values give bit-identical partials.  The scales must be finite and > 0 (not checked: they
+ * live on the device).  Errors as mla_decode_splitkv, plus INVALID_ARG for a NULL or
+ * misaligned scale pointer.
+ */
+mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                                         const int32_t* page_table_dev,
+                                         const int32_t* seq_lens_dev, int batch, int q_tokens,
+                                         int heads, int page_size, int max_pages,
+                                         int max_seq_len, const float* q_scale_dev,
+                                         const float* kv_scale_dev, float softmax_scale,
+                                         int num_splits, int rows_per_group,
+                                         uint16_t* partial_o_dev, float* partial_lse_dev,
+                                         int64_t partial_rows_capacity, void* stream);
+
+/*
  * Log-sum-exp merge of the split partials ([A/MLA] item (2)).  For each (b, r):
  *   M = max_s lse_s;  w_s = exp(lse_s - M);  O = v_scale * sum_s w_s O_s / sum_s w_s;
  *   lse = M + log(sum_s w_s)
@@ -154,6 +231,18 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
 mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* partial_lse_dev,
                                int batch, int num_splits, int q_tokens, int heads, float v_scale,
                                uint16_t* out_bf16_dev, float* out_lse_dev, void* stream);
+
+/*
+ * mla_splitkv_combine with v_scale read on the device from v_scale_dev[0] (a 4-byte aligned
+ * device float, finite and > 0; the KV scale the partials were computed with).  Output is
+ * bit-identical to mla_splitkv_combine with the same value.  Errors as mla_splitkv_combine,
+ * plus INVALID_ARG for a NULL or misaligned v_scale_dev.
+ */
+mla_status mla_splitkv_combine_dev_scale(const uint16_t* partial_o_dev,
+                                         const float* partial_lse_dev, int batch,
+                                         int num_splits, int q_tokens, int heads,
+                                         const float* v_scale_dev, uint16_t* out_bf16_dev,
+                                         float* out_lse_dev, void* stream);
 
 /*
  * Diagnostics, not part of the decode path: streams bytes of buf_dev from HBM (16-byte

@@ -31,6 +31,11 @@ def lib():
     L.mla_splitkv_combine.argtypes = [v, v, i, i, i, i, f, v, v, v]
     L.mla_splitkv_plan.argtypes = [i, i, i, i, i64, i, ctypes.POINTER(i), ctypes.POINTER(i),
                                    ctypes.POINTER(i64)]
+    L.mla_decode_splitkv_dev_scales.argtypes = [v, v, v, v, i, i, i, i, i, i, v, v, f, i, i, v,
+                                                v, i64, v]
+    L.mla_splitkv_combine_dev_scale.argtypes = [v, v, i, i, i, i, v, v, v, v]
+    L.mla_quantize_fp8_sat_dynamic.argtypes = [v, i, v, i64, v, v, i64, v]
+    L.mla_kv_append_fp8_sat.argtypes = [v, v, i64, v, v, i, i, i, i, f, v]
     return L
 
 
@@ -43,7 +48,9 @@ def header_functions():
 def test_header_declares_the_entry_points():
     names = header_functions()
     for n in ("mla_quantize_fp8_sat", "mla_decode_splitkv", "mla_splitkv_combine",
-              "mla_splitkv_plan", "mla_status_string"):
+              "mla_splitkv_plan", "mla_status_string", "mla_quantize_fp8_sat_dynamic",
+              "mla_kv_append_fp8_sat", "mla_decode_splitkv_dev_scales",
+              "mla_splitkv_combine_dev_scale"):
         assert n in names
 
 
@@ -121,6 +128,66 @@ def test_combine_rejects_bad_arguments(lib):
     assert c(FAKE, FAKE, 1, 4, 1, 16, float("nan"), FAKE, None, None) == INVALID
     assert c(FAKE, FAKE, 1, 5000, 1, 16, 1.0, FAKE, None, None) == UNSUPPORTED
     assert c(None, None, 0, 4, 1, 16, 1.0, None, None, None) == OK
+
+
+def test_dynamic_quantize_rejects_bad_arguments(lib):
+    q = lib.mla_quantize_fp8_sat_dynamic
+    W = 4096
+    assert q(FAKE, 0, FAKE, -1, FAKE, FAKE, W, None) == INVALID
+    assert q(FAKE, 2, FAKE, 10, FAKE, FAKE, W, None) == INVALID        # unknown source type
+    assert q(None, 0, FAKE, 10, FAKE, FAKE, W, None) == INVALID
+    assert q(FAKE, 0, None, 10, FAKE, FAKE, W, None) == INVALID
+    assert q(FAKE, 0, FAKE, 10, None, FAKE, W, None) == INVALID
+    assert q(FAKE, 0, FAKE, 10, FAKE, None, W, None) == INVALID
+    assert q(ctypes.c_void_p(0x1002), 0, FAKE, 10, FAKE, FAKE, W, None) == INVALID  # fp32 align
+    assert q(ctypes.c_void_p(0x1001), 1, FAKE, 10, FAKE, FAKE, W, None) == INVALID  # bf16 align
+    assert q(FAKE, 0, FAKE, 10, ctypes.c_void_p(0x1001), FAKE, W, None) == INVALID
+    assert q(FAKE, 0, FAKE, 10, FAKE, FAKE, W - 1, None) == WORKSPACE
+    assert q(None, 0, None, 0, None, None, 0, None) == OK                # empty: nothing enqueued
+
+
+def test_kv_append_rejects_bad_arguments(lib):
+    a = lib.mla_kv_append_fp8_sat
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, -1, 1, 64, 4, 1.0, None) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, -1, 64, 4, 1.0, None) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 0, 4, 1.0, None) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 0, 1.0, None) == INVALID
+    assert a(FAKE, FAKE, 0, FAKE, FAKE, 2, 1, 64, 4, 1.0, None) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 0.0, None) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, float("inf"), None) == INVALID
+    for k in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[k] = None
+        assert a(ptrs[0], ptrs[1], 8, ptrs[2], ptrs[3], 2, 1, 64, 4, 1.0, None) == INVALID
+    assert a(ctypes.c_void_p(0x1002), FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 1.0, None) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 1 << 16, 1 << 16, 64, 4, 1.0, None) == UNSUPPORTED
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 1 << 16, 1 << 16, 1.0, None) == UNSUPPORTED
+    assert a(None, None, 8, None, None, 0, 1, 64, 4, 1.0, None) == OK    # empty batch
+    assert a(None, None, 8, None, None, 2, 0, 64, 4, 1.0, None) == OK    # no new tokens
+
+
+def test_dev_scale_variants_reject_bad_arguments(lib):
+    d = lib.mla_decode_splitkv_dev_scales
+
+    def dec(qs=FAKE, ks=FAKE, sm=0.07, **kw):
+        a = dict(q=FAKE, B=1, P=64, cap=1 << 20)
+        a.update(kw)
+        return d(a["q"], FAKE, FAKE, FAKE, a["B"], 1, 16, a["P"], 4, 256, qs, ks, sm, 4, 128,
+                 FAKE, FAKE, a["cap"], None)
+    assert dec(qs=None) == INVALID
+    assert dec(ks=None) == INVALID
+    assert dec(qs=ctypes.c_void_p(0x1002)) == INVALID
+    assert dec(sm=0.0) == INVALID
+    assert dec(q=None) == INVALID
+    assert dec(P=48) == UNSUPPORTED
+    assert dec(cap=63) == WORKSPACE
+    assert dec(B=0, q=None) == OK
+    c = lib.mla_splitkv_combine_dev_scale
+    assert c(FAKE, FAKE, 1, 4, 1, 16, None, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, ctypes.c_void_p(0x1001), FAKE, None, None) == INVALID
+    assert c(None, FAKE, 1, 4, 1, 16, FAKE, FAKE, None, None) == INVALID
+    assert c(FAKE, FAKE, 1, 5000, 1, 16, FAKE, FAKE, None, None) == UNSUPPORTED
+    assert c(None, None, 0, 4, 1, 16, FAKE, None, None, None) == OK
 
 
 def _plan(lib, B, Sq, H, L, cu, total=0):

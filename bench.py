@@ -56,6 +56,9 @@ def _parse():
                          "(what a profiler run needs to see individual launches clearly)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the HBM probes, per-step percentiles and the split sweep")
+    ap.add_argument("--prep-only", action="store_true",
+                    help="time only the cache-preparation entry points (KV append, quantise "
+                         "with a device-derived scale) and print their JSON")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, --steps times (the "
                          "reference kernel that calibrates HBM byte counters), then exit")
@@ -90,7 +93,11 @@ def _time_graph(g, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_bytes=512 << 20):
+def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_bytes=512 << 20,
+                 dev_scales=False):
+    """One decode step = Q quantise + split-KV decode + combine, timed over `steps` steps.
+    dev_scales: Q's scale is derived on the device (mla_quantize_fp8_sat_dynamic) and the
+    decode and combine read both scales from device memory."""
     import torch
     import fp8_mla_split_amd as mla
     from fp8_mla_split_amd.workload import materialize
@@ -112,15 +119,24 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
     out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Sq, H), dtype=torch.float32, device="cuda")
 
+    qs_dev = torch.empty(1, dtype=torch.float32, device="cuda")
+    ks_dev = torch.tensor([dw.kv_scale], dtype=torch.float32, device="cuda")
+    ws = torch.empty(mla.QUANTIZE_DYNAMIC_WORKSPACE_BYTES // 4, dtype=torch.int32, device="cuda")
+    q_scale = qs_dev if dev_scales else dw.q_scale
+    kv_scale = ks_dev if dev_scales else dw.kv_scale
+
     def quantize():
-        mla.quantize_fp8_sat(q32, dw.q_scale, out=q8)
+        if dev_scales:
+            mla.quantize_fp8_sat_dynamic(q32, out=q8, scale=qs_dev, workspace=ws)
+        else:
+            mla.quantize_fp8_sat(q32, dw.q_scale, out=q8)
 
     def decode(i):
-        mla.decode_splitkv(q8, pools[i % copies], dw.page_table, dw.seq_lens, dw.q_scale,
-                           dw.kv_scale, w.softmax_scale, dw.max_seq_len, S, r, po, pl)
+        mla.decode_splitkv(q8, pools[i % copies], dw.page_table, dw.seq_lens, q_scale,
+                           kv_scale, w.softmax_scale, dw.max_seq_len, S, r, po, pl)
 
     def combine():
-        mla.splitkv_combine(po, pl, Sq, H, dw.kv_scale, out=out, out_lse=lse)
+        mla.splitkv_combine(po, pl, Sq, H, kv_scale, out=out, out_lse=lse)
 
     def step(i):
         quantize()
@@ -133,7 +149,8 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
 
     res = {"workload": w.name, "batch": B, "heads": H, "q_tokens": Sq,
            "context": int(dw.max_seq_len), "kv_tokens": dw.kv_tokens, "num_splits": S,
-           "rows_per_group": r, "kv_copies": copies, "timing": "eager" if eager else "hip_graph"}
+           "rows_per_group": r, "kv_copies": copies, "timing": "eager" if eager else "hip_graph",
+           "scales": "device (Q amax on the GPU)" if dev_scales else "host"}
     if eager:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = torch.cuda.Event(enable_timing=True)
@@ -243,6 +260,62 @@ def hbm_probes():
            "kv_quantize_us_per_gi_element": round(quant_us * 4, 1)}
     res["kv_quantize_frac_of_hbm_peak"] = round(res["kv_quantize_gbps"] / HBM_PEAK_GBPS, 4)
     del x, y, q8
+    torch.cuda.empty_cache()
+    return res
+
+
+def prep_probes():
+    """The cache-preparation entry points, each graph-timed in this run:
+    - KV append (mla_kv_append_fp8_sat) at the decode workloads' per-step shapes (one new row
+      per request at batch 32; 8 draft rows per request at batch 4) and in bulk (16 requests x
+      8192 rows: 4 B read + 1 B written per element, against the HBM roofline);
+    - the quantisation with a device-derived scale (mla_quantize_fp8_sat_dynamic) for one
+      step's Q at batch 1 and in bulk (2^28 elements, fp32 and bf16 sources).  Its two passes
+      read the source twice: algorithmic bytes are one read + one write, the executed traffic
+      two reads + one write; both rates are given."""
+    import torch
+    import fp8_mla_split_amd as mla
+    from synthetic import WORKLOADS, q_f32
+    res = {}
+    rng = np.random.default_rng(0)
+
+    def append_case(batch, t_new, max_pages, page_size=64, reps=200):
+        pages = batch * max_pages
+        pool = torch.zeros((pages, page_size, 576), dtype=torch.uint8, device="cuda")
+        table = torch.from_numpy(rng.permutation(pages).astype(np.int32).reshape(
+            batch, max_pages)).cuda()
+        lens = torch.from_numpy(rng.integers(t_new, max_pages * page_size + 1, size=batch)
+                                .astype(np.int32)).cuda()
+        new = torch.randn((batch, t_new, 576), device="cuda")
+        us = _time_fn_graph(lambda: mla.kv_append_fp8_sat(new, pool, table, lens, 0.01), reps)
+        return us, batch * t_new * 576
+    us, n = append_case(32, 1, 2048)
+    res["kv_append_b32_t1_us"] = round(us, 2)
+    us, n = append_case(4, 8, 16384)
+    res["kv_append_b4_t8_us"] = round(us, 2)
+    us, n = append_case(16, 8192, 129, reps=20)
+    res["kv_append_bulk_b16_t8192"] = {"us": round(us, 1), "gbps": round(5 * n / (us * 1e3), 1),
+                                       "frac_of_hbm_peak": round(5 * n / (us * 1e3)
+                                                                 / HBM_PEAK_GBPS, 4)}
+    ws = torch.empty(mla.QUANTIZE_DYNAMIC_WORKSPACE_BYTES // 4, dtype=torch.int32, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    q = torch.from_numpy(q_f32(WORKLOADS["b1_128k"])).cuda()
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
+    res["dynamic_quantize_q_b1_us"] = round(_time_fn_graph(
+        lambda: mla.quantize_fp8_sat_dynamic(q, out=q8, scale=sc, workspace=ws), 200), 2)
+    res["host_scale_quantize_q_b1_us"] = round(_time_fn_graph(
+        lambda: mla.quantize_fp8_sat(q, 0.01, out=q8), 200), 2)
+    n = 1 << 28
+    for name, dt, esz in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+        x = torch.randn(n, device="cuda").to(dt)
+        y = torch.empty(n, dtype=torch.uint8, device="cuda")
+        us = _time_fn_graph(lambda: mla.quantize_fp8_sat_dynamic(x, out=y, scale=sc,
+                                                                 workspace=ws), 5)
+        res[f"dynamic_quantize_bulk_{name}"] = {
+            "us_per_gi_element": round(us * 4, 1),
+            "algorithmic_gbps": round((esz + 1) * n / (us * 1e3), 1),
+            "executed_gbps": round((2 * esz + 1) * n / (us * 1e3), 1)}
+        del x, y
     torch.cuda.empty_cache()
     return res
 
@@ -413,6 +486,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     sys.path.insert(0, ROOT)
+    if a.prep_only:
+        print(json.dumps({"cache_prep": prep_probes()}), flush=True)
+        return
     t_wall = time.time()
     main_res = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager)
     print(f"[bench] {a.workload}: {main_res['us_per_step']:.2f} us/step (decode "
@@ -429,7 +505,18 @@ def main():
     if not a.no_extras:
         extras = {"hbm_probes": hbm_probes(),
                   "step_percentiles": step_percentiles(a.workload),
-                  "split_sweep": split_sweep(a.workload)}
+                  "split_sweep": split_sweep(a.workload),
+                  "cache_prep": prep_probes()}
+        dyn = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager,
+                           dev_scales=True)
+        extras["device_scale_step"] = {k: round(dyn[k], 3) for k in (
+            "us_per_step", "quantize_q_us", "decode_us", "combine_us")}
+        extras["device_scale_step"]["note"] = (
+            "the same step with Q's scale derived on the GPU and both scales read by the "
+            "decode and combine from device memory")
+        print(f"[bench] device-scale step: {dyn['us_per_step']:.2f} us (Q amax+quantize "
+              f"{dyn['quantize_q_us']:.2f} us); cache prep: "
+              + json.dumps(extras["cache_prep"]), file=sys.stderr, flush=True)
         pr = extras["hbm_probes"]
         print(f"[bench] measured HBM: read {pr['read_gbps']:.0f} GB/s, copy {pr['copy_gbps']:.0f} "
               f"GB/s, KV quantize {pr['kv_quantize_gbps']:.0f} GB/s; step p10/p50/p90 "

@@ -29,6 +29,9 @@ Pinning (what each function is checked against, in ``tests/test_oracle_*``):
 * ``attention_fp64``     closed forms on tiny inputs; float64
                          ``scaled_dot_product_attention`` with an explicit
                          causal mask; paged == contiguous; head independence.
+                         Per-request query counts (``q_lens``): a hand-written
+                         loop over a 2-of-4-token request, empty requests, and
+                         equality with a call holding only those slots.
 * ``split_partials_fp64`` / ``combine_fp64``  S = 1 identity, the two-split
                          closed form, and split-count independence.
 * ``bf16_bits_to_f32``   torch's bfloat16 -> float32 conversion on all 65536

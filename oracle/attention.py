@@ -58,7 +58,8 @@ def attention_fp64(q8: np.ndarray, q_scale: float, kv_pool8: np.ndarray, kv_scal
                    page_table: np.ndarray, seq_lens: np.ndarray, page_size: int,
                    softmax_scale: float, requests: Optional[Sequence[int]] = None,
                    heads: Optional[Sequence[int]] = None,
-                   token_range: Optional[Sequence[int]] = None):
+                   token_range: Optional[Sequence[int]] = None,
+                   q_lens: Optional[Sequence[int]] = None):
     """Unsplit decode attention.
 
     q8: uint8 ``[B, Sq, H, 576]``; kv_pool8: uint8 ``[pages, P, 576]``;
@@ -67,6 +68,10 @@ def attention_fp64(q8: np.ndarray, q_scale: float, kv_pool8: np.ndarray, kv_scal
     only those, in the given order).  ``token_range=(lo, hi)`` restricts every
     query to logical positions ``[lo, hi)`` intersected with its causal window
     (used to state one split of the split form).
+    ``q_lens[b]`` (clamped to [0, Sq]) gives request b its own number of query tokens:
+    they are the first q_lens[b] slots of ``q8[b]`` and the last q_lens[b] positions of
+    its context (a verify step with a different number of draft tokens per request,
+    [A/MLA] opening paragraph); the remaining slots see nothing (O = 0, lse = -inf).
     Returns ``(O [b, Sq, h, 512], lse [b, Sq, h])`` in float64.
     """
     B, Sq, H, _ = q8.shape
@@ -79,8 +84,9 @@ def attention_fp64(q8: np.ndarray, q_scale: float, kv_pool8: np.ndarray, kv_scal
         kd = decode_e4m3(gather_kv_rows(kv_pool8, page_table, b, L, page_size)) * float(kv_scale)
         vd = kd[:, :D_V]
         qd = decode_e4m3(q8[b][:, hs, :]) * float(q_scale)           # [Sq, h, 576]
-        for t in range(Sq):
-            hi = L - Sq + t + 1                                        # visible: [0, hi)
+        nq = Sq if q_lens is None else min(max(int(q_lens[b]), 0), Sq)
+        for t in range(nq):
+            hi = L - nq + t + 1                                        # visible: [0, hi)
             lo = 0
             if token_range is not None:
                 lo, hi = max(lo, token_range[0]), min(hi, token_range[1])

@@ -230,3 +230,49 @@ def test_empty_chunk_partial_is_minus_inf():
     q8, qs, kv8, ks, pool, table, P, lens = _rand_case(B=1, Sq=1, H=2, L=(64,))
     po, pl = split_partials_fp64(q8, qs, pool, ks, table, lens, P, SM, [[(0, 64), (64, 64)]])
     assert np.all(pl[0, 1] == -np.inf) and np.all(po[0, 1] == 0)
+
+
+# ------------------------------------------ per-request query counts (ragged verify)
+
+def test_per_request_query_counts_by_hand():
+    """4 query slots; request 0 has 2 tokens over a 3-position context, request 1 none,
+    request 2 all 4.  Request 0's token 0 sees positions 0-1 and token 1 sees 0-2 (written
+    out with loops below); its slots 2 and 3, and all of request 1, see nothing."""
+    q8, qs, kv8, ks, pool, table, P, lens = _rand_case(B=3, Sq=4, H=2, L=(3, 9, 40), seed=5)
+    qlen = np.array([2, 0, 4], np.int32)
+    o, lse = attention_fp64(q8, qs, pool, ks, table, lens, P, SM, q_lens=qlen)
+    k = decode_e4m3(kv8[0]) * float(ks)
+    for t, visible in ((0, 2), (1, 3)):
+        for h in range(2):
+            qd = decode_e4m3(q8[0, t, h]) * float(qs)
+            z = [SM * sum(qd[d] * k[n, d] for d in range(576)) for n in range(visible)]
+            m = max(z)
+            w = [math.exp(x - m) for x in z]
+            ref = [sum(w[n] * k[n, c] for n in range(visible)) / sum(w) for c in range(512)]
+            assert np.allclose(o[0, t, h], ref, rtol=0, atol=1e-12)
+            assert abs(lse[0, t, h] - (m + math.log(sum(w)))) <= 1e-12
+    assert np.all(o[0, 2:] == 0) and np.all(lse[0, 2:] == -np.inf)
+    assert np.all(o[1] == 0) and np.all(lse[1] == -np.inf)
+    full_o, full_l = attention_fp64(q8, qs, pool, ks, table, lens, P, SM, requests=[2])
+    assert np.array_equal(o[2], full_o[0]) and np.array_equal(lse[2], full_l[0])
+
+
+def test_full_query_counts_change_nothing():
+    q8, qs, kv8, ks, pool, table, P, lens = _rand_case(B=2, Sq=3, H=4, L=(130, 4), seed=6)
+    a = attention_fp64(q8, qs, pool, ks, table, lens, P, SM)
+    b = attention_fp64(q8, qs, pool, ks, table, lens, P, SM, q_lens=[3, 3])
+    c = attention_fp64(q8, qs, pool, ks, table, lens, P, SM, q_lens=[7, 99])   # clamped
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+
+
+def test_short_request_is_the_same_as_a_call_with_fewer_slots():
+    """A request with k of Sq tokens: its first k slots equal a call whose q8 holds only
+    those k slots (the causal window shifts with k, not with Sq)."""
+    q8, qs, kv8, ks, pool, table, P, lens = _rand_case(B=1, Sq=8, H=2, L=(300,), seed=7)
+    for k in (1, 3, 5):
+        o, lse = attention_fp64(q8, qs, pool, ks, table, lens, P, SM, q_lens=[k])
+        o2, lse2 = attention_fp64(np.ascontiguousarray(q8[:, :k]), qs, pool, ks, table, lens, P,
+                                  SM)
+        assert np.array_equal(o[:, :k], o2) and np.array_equal(lse[:, :k], lse2)
+        assert np.all(lse[:, k:] == -np.inf)

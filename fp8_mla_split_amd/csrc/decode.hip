@@ -277,7 +277,7 @@ struct KPair {
   i32x4 a0, a1, b0, b1;
 };
 
-template <bool kPairPages, bool kDevScale>
+template <bool kPairPages, bool kDevScale, bool kRagged>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
@@ -338,7 +338,15 @@ void decode_kernel(const DecodeParams p) {
   const int pt_hint = ptrow[(uint32_t)min((int)fast_div((uint32_t)(s * p.tiles_hint), p.div_tpp),
                                           p.max_pages - 1)];
   int L = seq_lens[b];
-  asm volatile("" ::"s"(L), "s"(pt_hint));  // both loads go out before either is waited for
+  // query tokens of this request: all q_tokens, or its own count when requests differ
+  int qlen = p.q_tokens;
+  if constexpr (kRagged) {
+    qlen = ((const __attribute__((address_space(4))) int32_t*)p.q_lens)[b];
+    asm volatile("" ::"s"(L), "s"(pt_hint), "s"(qlen));  // all three loads go out together
+    qlen = qlen < 0 ? 0 : (qlen > p.q_tokens ? p.q_tokens : qlen);
+  } else {
+    asm volatile("" ::"s"(L), "s"(pt_hint));  // both loads go out before either is waited for
+  }
   // scales kept on the device (written by an earlier kernel on the stream): loaded here, used
   // first by the softmax of step 0, long after they land
   float qs_dev = 0.f, ks_dev = 0.f;
@@ -510,9 +518,16 @@ void decode_kernel(const DecodeParams p) {
   // last visible position of the row (bottom-right causal); rows past M are never stored
   // (computed for every lane, then selected: a branch here would make the compiler spill
   // around it and wait for the Q DMA)
-  const int lim_r = L - p.q_tokens + (int)fast_div((uint32_t)R, p.div_heads);
+  // A row whose query token t is past its request's count sees nothing (lim = -1), like a
+  // query with no visible position: its lse is -inf.
+  const int t_r = (int)fast_div((uint32_t)R, p.div_heads);
+  const int lim_r = kRagged ? (t_r < qlen ? L - qlen + t_r : -1) : L - qlen + t_r;
   const int lim = row_ok ? lim_r : 0x7FFFFFFF;
-  const int lim_min = L - p.q_tokens + (int)fast_div((uint32_t)wrow0, p.div_heads);
+  int lim_min = L - qlen + (int)fast_div((uint32_t)wrow0, p.div_heads);
+  if constexpr (kRagged) {  // the wave's smallest limit is -1 if it holds an absent row
+    const int t_hi = (int)fast_div((uint32_t)min(wrow0 + 31, M - 1), p.div_heads);
+    if (t_hi >= qlen) lim_min = -1;
+  }
   const int nsteps = (ntiles + 1) / 2;
   // Steps 0 .. nplain-1 need no masking: both tiles in the chunk and every position visible
   // to every row of this wave (tile 2j + 1 ends at (t_begin + 2j + 2) * 32 - 1 <= lim_min).
@@ -917,15 +932,18 @@ hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t 
   const int64_t blocks = ((units + 7) / 8) * 8 * p.groups;
   // an even number of tiles per page (and pages under 4 GiB) takes the paired-tile cursor
   const bool paired = (p.page_size / kTile) % 2 == 0 && p.page_bytes < (int64_t(1) << 32);
-  const bool dev = p.q_scale_dev != nullptr;
-  if (paired && !dev)
-    decode_kernel<true, false><<<(unsigned)blocks, 256, 0, s>>>(p);
-  else if (!dev)
-    decode_kernel<false, false><<<(unsigned)blocks, 256, 0, s>>>(p);
-  else if (paired)
-    decode_kernel<true, true><<<(unsigned)blocks, 256, 0, s>>>(p);
-  else
-    decode_kernel<false, true><<<(unsigned)blocks, 256, 0, s>>>(p);
+  const int v = (paired ? 1 : 0) | (p.q_scale_dev != nullptr ? 2 : 0) | (p.q_lens ? 4 : 0);
+  const dim3 grid((unsigned)blocks), block(256);
+  switch (v) {
+    case 0: decode_kernel<false, false, false><<<grid, block, 0, s>>>(p); break;
+    case 1: decode_kernel<true, false, false><<<grid, block, 0, s>>>(p); break;
+    case 2: decode_kernel<false, true, false><<<grid, block, 0, s>>>(p); break;
+    case 3: decode_kernel<true, true, false><<<grid, block, 0, s>>>(p); break;
+    case 4: decode_kernel<false, false, true><<<grid, block, 0, s>>>(p); break;
+    case 5: decode_kernel<true, false, true><<<grid, block, 0, s>>>(p); break;
+    case 6: decode_kernel<false, true, true><<<grid, block, 0, s>>>(p); break;
+    default: decode_kernel<true, true, true><<<grid, block, 0, s>>>(p); break;
+  }
   return hipGetLastError();
 }
 

@@ -54,6 +54,9 @@ struct DecodeParams {
   const float* q_scale_dev;
   const float* kv_scale_dev;
   float softmax_scale;
+  // per-request query-token counts (NULL: every request has q_tokens); device values are
+  // clamped to [0, q_tokens]
+  const int32_t* q_lens;
 };
 
 // c2 from the three scales: products in double, one rounding to float (host and device alike)

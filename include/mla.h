@@ -214,6 +214,33 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
                                          int64_t partial_rows_capacity, void* stream);
 
 /*
+ * The general form of the decode call: mla_decode_splitkv plus
+ *   q_lens_dev   int32 [B] (device) or NULL.  Request b has q_lens_dev[b] query tokens
+ *                (device values are clamped to [0, q_tokens]): the verify step of block
+ *                speculative decoding ([A/MLA], opening paragraph: every decode step drafts a
+ *                few tokens, then verifies them) with a different number of draft tokens per
+ *                request.  Its tokens are the
+ *                first q_lens_dev[b] of the q_tokens slots of q8 and are the last
+ *                q_lens_dev[b] positions of its context: token t sees positions
+ *                0 .. L_b - q_lens_dev[b] + t.  Rows of slots t >= q_lens_dev[b] see nothing:
+ *                their partial lse is -inf in every split, so the combine gives O = 0 and
+ *                lse = -inf for them.  NULL: every request has q_tokens tokens.
+ *   q_scale_dev, kv_scale_dev  both NULL (q_scale and kv_scale are used) or both device
+ *                floats (as mla_decode_splitkv_dev_scales).
+ * Errors as mla_decode_splitkv, plus INVALID_ARG for exactly one NULL scale pointer or a
+ * misaligned pointer.
+ */
+mla_status mla_decode_splitkv_ex(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                                 const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                                 const int32_t* q_lens_dev, int batch, int q_tokens, int heads,
+                                 int page_size, int max_pages, int max_seq_len, float q_scale,
+                                 float kv_scale, const float* q_scale_dev,
+                                 const float* kv_scale_dev, float softmax_scale, int num_splits,
+                                 int rows_per_group, uint16_t* partial_o_dev,
+                                 float* partial_lse_dev, int64_t partial_rows_capacity,
+                                 void* stream);
+
+/*
  * Log-sum-exp merge of the split partials ([A/MLA] item (2)).  For each (b, r):
  *   M = max_s lse_s;  w_s = exp(lse_s - M);  O = v_scale * sum_s w_s O_s / sum_s w_s;
  *   lse = M + log(sum_s w_s)

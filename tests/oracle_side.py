@@ -72,13 +72,16 @@ def q8_request(w: Workload, b: int, q_scale) -> np.ndarray:
 
 
 def attention_request(w: Workload, b: int, L: int, q8_b: np.ndarray, q_scale, kv8: np.ndarray,
-                      kv_scale, heads: Optional[Sequence[int]] = None):
-    """Oracle O [Sq, h, 512] and lse [Sq, h] of one request, through a one-page pool."""
+                      kv_scale, heads: Optional[Sequence[int]] = None,
+                      q_len: Optional[int] = None):
+    """Oracle O [Sq, h, 512] and lse [Sq, h] of one request, through a one-page pool;
+    q_len: the request's own number of query tokens (default: all Sq slots)."""
     P = max(32, -(-L // 32) * 32)
     pool_ = np.zeros((1, P, D_KV), np.uint8)
     pool_[0, :L] = kv8
     o, lse = attention_fp64(q8_b[None], q_scale, pool_, kv_scale, np.zeros((1, 1), np.int32),
-                            np.array([L], np.int32), P, w.softmax_scale, heads=heads)
+                            np.array([L], np.int32), P, w.softmax_scale, heads=heads,
+                            q_lens=None if q_len is None else [q_len])
     return o[0], lse[0]
 
 

@@ -34,6 +34,8 @@ def lib():
     L.mla_decode_splitkv_dev_scales.argtypes = [v, v, v, v, i, i, i, i, i, i, v, v, f, i, i, v,
                                                 v, i64, v]
     L.mla_splitkv_combine_dev_scale.argtypes = [v, v, i, i, i, i, v, v, v, v]
+    L.mla_decode_splitkv_ex.argtypes = [v, v, v, v, v, i, i, i, i, i, i, f, f, v, v, f, i, i, v,
+                                        v, i64, v]
     L.mla_quantize_fp8_sat_dynamic.argtypes = [v, i, v, i64, v, v, i64, v]
     L.mla_kv_append_fp8_sat.argtypes = [v, v, i64, v, v, i, i, i, i, f, v]
     return L
@@ -50,7 +52,7 @@ def test_header_declares_the_entry_points():
     for n in ("mla_quantize_fp8_sat", "mla_decode_splitkv", "mla_splitkv_combine",
               "mla_splitkv_plan", "mla_status_string", "mla_quantize_fp8_sat_dynamic",
               "mla_kv_append_fp8_sat", "mla_decode_splitkv_dev_scales",
-              "mla_splitkv_combine_dev_scale"):
+              "mla_splitkv_combine_dev_scale", "mla_decode_splitkv_ex"):
         assert n in names
 
 
@@ -188,6 +190,28 @@ def test_dev_scale_variants_reject_bad_arguments(lib):
     assert c(None, FAKE, 1, 4, 1, 16, FAKE, FAKE, None, None) == INVALID
     assert c(FAKE, FAKE, 1, 5000, 1, 16, FAKE, FAKE, None, None) == UNSUPPORTED
     assert c(None, None, 0, 4, 1, 16, FAKE, None, None, None) == OK
+
+
+def test_decode_ex_rejects_bad_arguments(lib):
+    d = lib.mla_decode_splitkv_ex
+
+    def dec(ql=FAKE, qsd=None, ksd=None, qs=1.0, ks=1.0, **kw):
+        a = dict(q=FAKE, B=1, P=64, cap=1 << 20, Sq=8)
+        a.update(kw)
+        return d(a["q"], FAKE, FAKE, FAKE, ql, a["B"], a["Sq"], 16, a["P"], 4, 256, qs, ks, qsd,
+                 ksd, 0.07, 4, 128, FAKE, FAKE, a["cap"], None)
+    assert dec(qsd=FAKE) == INVALID                     # one scale pointer without the other
+    assert dec(ksd=FAKE) == INVALID
+    assert dec(ql=ctypes.c_void_p(0x1002)) == INVALID   # q_lens misaligned
+    assert dec(qs=0.0) == INVALID                       # host scales checked when used
+    # with device scales the host values are not used: the call gets as far as the
+    # workspace check (which fails here, so nothing is launched)
+    assert dec(qs=0.0, qsd=FAKE, ksd=FAKE, cap=8 * 16 * 4 - 1) == WORKSPACE
+    assert dec(q=None) == INVALID
+    assert dec(P=48) == UNSUPPORTED
+    assert dec(cap=8 * 16 * 4 - 1) == WORKSPACE
+    assert dec(B=0, q=None) == OK
+    assert dec(B=0, q=None, ql=None) == OK
 
 
 def _plan(lib, B, Sq, H, L, cu, total=0):

@@ -48,6 +48,9 @@ def _parse():
     ap.add_argument("--also", default="b16_128k",
                     help="second workload reported alongside ('' = none)")
     ap.add_argument("--splits", type=int, default=0, help="0 = planner")
+    ap.add_argument("--q-lens", default="",
+                    help="comma-separated query-token count per request (verify step with a "
+                         "different number of draft tokens per request); empty = all q_tokens")
     ap.add_argument("--rows-per-group", type=int, default=0, help="0 = planner")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -94,7 +97,7 @@ def _time_graph(g, reps):
 
 
 def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_bytes=512 << 20,
-                 dev_scales=False):
+                 dev_scales=False, q_lens=None):
     """One decode step = Q quantise + split-KV decode + combine, timed over `steps` steps.
     dev_scales: Q's scale is derived on the device (mla_quantize_fp8_sat_dynamic) and the
     decode and combine read both scales from device memory."""
@@ -131,9 +134,15 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
         else:
             mla.quantize_fp8_sat(q32, dw.q_scale, out=q8)
 
+    ql = None
+    if q_lens:
+        if len(q_lens) != B:
+            raise SystemExit(f"--q-lens needs {B} counts for {w.name}")
+        ql = torch.tensor(q_lens, dtype=torch.int32, device="cuda")
+
     def decode(i):
         mla.decode_splitkv(q8, pools[i % copies], dw.page_table, dw.seq_lens, q_scale,
-                           kv_scale, w.softmax_scale, dw.max_seq_len, S, r, po, pl)
+                           kv_scale, w.softmax_scale, dw.max_seq_len, S, r, po, pl, q_lens=ql)
 
     def combine():
         mla.splitkv_combine(po, pl, Sq, H, kv_scale, out=out, out_lse=lse)
@@ -151,6 +160,8 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
            "context": int(dw.max_seq_len), "kv_tokens": dw.kv_tokens, "num_splits": S,
            "rows_per_group": r, "kv_copies": copies, "timing": "eager" if eager else "hip_graph",
            "scales": "device (Q amax on the GPU)" if dev_scales else "host"}
+    if q_lens:
+        res["q_lens"] = list(q_lens)
     if eager:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = torch.cuda.Event(enable_timing=True)
@@ -194,8 +205,12 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
     # QK^T + PV, algorithmic: 2 * 1088 flops per (query row, cached token) of each request
     # (kv_tokens already sums the requests' lengths); the kernel executes 50 FP8 MFMAs of
     # 32x32x64 per 32 rows x 64 tokens (P.V twice, hi and lo): 3200 flops per (row, token)
-    flops = 2.0 * Sq * H * dw.kv_tokens * (576 + 512)
-    flops_exec = 3200.0 * Sq * H * dw.kv_tokens
+    # with per-request counts only the present query rows count as algorithmic work (the
+    # kernel skips row groups that hold no present row)
+    row_tokens = Sq * dw.kv_tokens if not q_lens else float(np.dot(
+        np.clip(np.asarray(q_lens), 0, Sq), dw.seq_lens_host.astype(np.float64)))
+    flops = 2.0 * H * row_tokens * (576 + 512)
+    flops_exec = 3200.0 * H * row_tokens
     res.update({
         "us_per_step": step_us,
         "quantize_q_us": q_us, "decode_us": dec_us, "combine_us": comb_us,
@@ -490,7 +505,9 @@ def main():
         print(json.dumps({"cache_prep": prep_probes()}), flush=True)
         return
     t_wall = time.time()
-    main_res = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager)
+    q_lens = [int(x) for x in a.q_lens.split(",")] if a.q_lens else None
+    main_res = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager,
+                            q_lens=q_lens)
     print(f"[bench] {a.workload}: {main_res['us_per_step']:.2f} us/step (decode "
           f"{main_res['decode_us']:.2f} us, {main_res['decode_gbps']:.0f} GB/s; combine "
           f"{main_res['combine_us']:.2f} us; Q quantize {main_res['quantize_q_us']:.2f} us)",
@@ -545,7 +562,8 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/KV, per-tensor scales)",
         "config": {k: main_res[k] for k in ("workload", "batch", "heads", "q_tokens", "context",
                                             "num_splits", "rows_per_group", "kv_copies",
-                                            "timing")},
+                                            "timing")} | (
+            {"q_lens": main_res["q_lens"]} if "q_lens" in main_res else {}),
         "kv_read_gbps_step": round(main_res["step_kv_gbps"], 1),
         "kv_read_pct_of_peak_step": round(100 * main_res["step_kv_gbps"] / HBM_PEAK_GBPS, 2),
         "breakdown_us": {k: round(main_res[k], 3) for k in ("quantize_q_us", "decode_us",

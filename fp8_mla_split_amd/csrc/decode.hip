@@ -363,7 +363,9 @@ void decode_kernel(const DecodeParams p) {
   const int ntiles = max(min(t_begin + per, ntiles_all) - t_begin, 0);
 
   const int64_t prow = (int64_t)(b * S + s) * M;  // first partial row of this (b, s)
-  if (ntiles == 0) {
+  // nothing to compute: an empty chunk, or (per-request counts) a row group whose first row
+  // already belongs to a query slot past the request's count, so every row of it is absent
+  if (ntiles == 0 || (kRagged && (int)fast_div((uint32_t)row0, p.div_heads) >= qlen)) {
     wait_vmcnt<0>();  // the Q DMA lands before the workgroup's LDS is released
     for (int i = threadIdx.x; i < kRows; i += 256)
       if (row0 + i < M) p.partial_lse[prow + row0 + i] = -INFINITY;

@@ -222,3 +222,51 @@ def test_dev_scales_on_paged_causal_case():
     assert np.array_equal(got[0].view(np.uint16), ref[0].view(np.uint16))
     assert np.array_equal(got[2], ref[2]) and np.array_equal(got[3], ref[3])
     _compare(dw, got[2], got[3], _oracle(dw, [0, 1, 2]))
+
+
+def test_device_scale_step_replays_in_a_graph():
+    """Append + Q amax/quantise + device-scale decode + combine captured in one HIP graph:
+    every replay (with eager work and synchronisations between replays) gives the eager
+    result bit for bit; nothing in the chain needs clearing before a replay."""
+    w = Workload("graph_dev", batch=2, heads=64, q_tokens=1, context=None, context_range=(1, 1),
+                 page_size=64, permuted_pool=True, seed=41)
+    lens = np.array([1500, 2100], np.int32)
+    dw = materialize(w, seq_lens=lens, keep_f32=True)
+    q32 = torch.from_numpy(q_f32(w)).cuda()
+    last = torch.stack([dw.kv_f32[b][int(lens[b]) - 1] for b in range(2)])[:, None].contiguous()
+    ks = torch.tensor([dw.kv_scale], dtype=torch.float32, device="cuda")
+    q8 = torch.empty(q32.shape, dtype=torch.uint8, device="cuda")
+    qs = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(mla.QUANTIZE_DYNAMIC_WORKSPACE_BYTES // 4, dtype=torch.int32, device="cuda")
+    S = 5
+    po = torch.empty((2, S, 64, 512), dtype=torch.float16, device="cuda")
+    pl = torch.empty((2, S, 64), dtype=torch.float32, device="cuda")
+    out = torch.empty((2, 1, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((2, 1, 64), dtype=torch.float32, device="cuda")
+
+    def step():
+        mla.kv_append_fp8_sat(last, dw.kv_pool8, dw.page_table, dw.seq_lens, dw.kv_scale)
+        mla.quantize_fp8_sat_dynamic(q32, out=q8, scale=qs, workspace=ws)
+        mla.decode_splitkv(q8, dw.kv_pool8, dw.page_table, dw.seq_lens, qs, ks, w.softmax_scale,
+                           dw.max_seq_len, S, 0, po, pl)
+        mla.splitkv_combine(po, pl, 1, 64, ks, out=out, out_lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        qs.fill_(-1.0)
+        ws.fill_(0x7FFFFFFF)                       # stale maxima must not leak into the scale
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), rep
+        assert torch.equal(lse, ref_l), rep
+        assert np.float32(qs.item()) == np.float32(dw.q_scale)
+    _compare(dw, _bf16(out), lse.cpu().numpy(), _oracle(dw, [0, 1]))

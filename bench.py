@@ -335,6 +335,60 @@ def prep_probes():
     return res
 
 
+def context_parallel_share(key="b1_128k", gpus=8, n=100, sweep=(16, 32, 64, 0)):
+    """One GPU's share of a context-parallel decode of one request, at its real shape: the
+    request's KV cut into `gpus` contiguous shards (here 16,384 of the 131,072 positions),
+    each shard decoded with S_local splits, and the combine over the gpus x S_local partials
+    that an all-gather would assemble.  S_local runs over `sweep` (0 = the planner's choice
+    for the shard's length, which does not know about the cross-GPU combine).  The shard
+    rotates over more than 512 MiB of KV so that no cache holds it; the all-gather itself
+    needs a second GPU and is not timed (its size per GPU is reported)."""
+    import torch
+    import fp8_mla_split_amd as mla
+    from fp8_mla_split_amd.workload import materialize
+    from synthetic import WORKLOADS
+    w = WORKLOADS[key]
+    dw = materialize(w)
+    L = int(dw.seq_lens_host[0])
+    Ls = L // gpus
+    copies = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(8)]
+    shards = [c[0, :L].view(gpus, Ls, 576) for c in copies]
+    lens = torch.full((1,), Ls, dtype=torch.int32, device="cuda")
+    tables = [torch.full((1, 1), g, dtype=torch.int32, device="cuda") for g in range(gpus)]
+    out = torch.empty((1, 1, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 1, w.heads), dtype=torch.float32, device="cuda")
+    planned = mla.splitkv_plan(1, 1, w.heads, Ls).num_splits
+    rows = []
+    for S in sweep:
+        S = S or planned
+        po = torch.empty((1, gpus * S, w.heads, 512), dtype=torch.float16, device="cuda")
+        pl = torch.empty((1, gpus * S, w.heads), dtype=torch.float32, device="cuda")
+        k = [0]
+
+        def decode_share():
+            i = k[0]
+            k[0] += 1
+            c, g = i % len(shards), (i // len(shards)) % gpus
+            mla.decode_splitkv(dw.q8, shards[c], tables[g], lens, dw.q_scale, dw.kv_scale,
+                               w.softmax_scale, Ls, S, 0, po[:, :S], pl[:, :S])
+        for g in range(gpus):  # every shard's slice filled once, as the all-gather would
+            mla.decode_splitkv(dw.q8, shards[0], tables[g], lens, dw.q_scale, dw.kv_scale,
+                               w.softmax_scale, Ls, S, 0, po[:, g * S:(g + 1) * S],
+                               pl[:, g * S:(g + 1) * S])
+        dec_us = _time_fn_graph(decode_share, n)
+        comb_us = _time_fn_graph(lambda: mla.splitkv_combine(po, pl, 1, w.heads, dw.kv_scale,
+                                                             out=out, out_lse=lse), n)
+        rows.append({"splits_per_shard": S, "planner": S == planned,
+                     "share_decode_us": round(dec_us, 2), "combine_us": round(comb_us, 2),
+                     "all_gather_bytes_per_gpu": S * w.heads * (512 * 2 + 4)})
+        del po, pl
+    del copies, shards, dw
+    torch.cuda.empty_cache()
+    return {"gpus": gpus, "shard_tokens": Ls, "rows": rows,
+            "note": "decode of one GPU's shard + combine over all shards' partials; the "
+                    "all-gather of the partials between GPUs is not measured (one GPU)"}
+
+
 def step_percentiles(key, n_steps=60):
     """p10 / p50 / p90 of single decode steps (quantize + decode + combine), each a one-step
     HIP graph on its own KV copy (so no step finds its KV cached), timed with events."""
@@ -523,7 +577,8 @@ def main():
         extras = {"hbm_probes": hbm_probes(),
                   "step_percentiles": step_percentiles(a.workload),
                   "split_sweep": split_sweep(a.workload),
-                  "cache_prep": prep_probes()}
+                  "cache_prep": prep_probes(),
+                  "context_parallel_share": context_parallel_share()}
         dyn = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager,
                            dev_scales=True)
         extras["device_scale_step"] = {k: round(dyn[k], 3) for k in (

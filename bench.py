@@ -337,12 +337,13 @@ def prep_probes():
 
 def context_parallel_share(key="b1_128k", gpus=8, n=100, sweep=(16, 32, 64, 0)):
     """One GPU's share of a context-parallel decode of one request, at its real shape: the
-    request's KV cut into `gpus` contiguous shards (here 16,384 of the 131,072 positions),
-    each shard decoded with S_local splits, and the combine over the gpus x S_local partials
-    that an all-gather would assemble.  S_local runs over `sweep` (0 = the planner's choice
-    for the shard's length, which does not know about the cross-GPU combine).  The shard
-    rotates over more than 512 MiB of KV so that no cache holds it; the all-gather itself
-    needs a second GPU and is not timed (its size per GPU is reported)."""
+    request's KV cut into `gpus` contiguous shards (here 16,384 of the 131,072 positions);
+    a GPU decodes its shard with S_local splits and merges them into one partial row per
+    query row (mla_splitkv_combine_partial); the GPUs would all-gather those rows (reported:
+    Sq*H*1028 bytes per GPU, not timed, it needs a second GPU) and run the final combine over
+    the `gpus` merged partials (timed).  S_local runs over `sweep` (0 = the planner's choice
+    for the shard's length).  The shard rotates over more than 512 MiB of KV so that no
+    cache holds it."""
     import torch
     import fp8_mla_split_amd as mla
     from fp8_mla_split_amd.workload import materialize
@@ -351,18 +352,21 @@ def context_parallel_share(key="b1_128k", gpus=8, n=100, sweep=(16, 32, 64, 0)):
     dw = materialize(w)
     L = int(dw.seq_lens_host[0])
     Ls = L // gpus
+    R = w.q_tokens * w.heads
     copies = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(8)]
     shards = [c[0, :L].view(gpus, Ls, 576) for c in copies]
     lens = torch.full((1,), Ls, dtype=torch.int32, device="cuda")
     tables = [torch.full((1, 1), g, dtype=torch.int32, device="cuda") for g in range(gpus)]
-    out = torch.empty((1, 1, w.heads, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((1, 1, w.heads), dtype=torch.float32, device="cuda")
-    planned = mla.splitkv_plan(1, 1, w.heads, Ls).num_splits
+    out = torch.empty((1, w.q_tokens, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, w.q_tokens, w.heads), dtype=torch.float32, device="cuda")
+    go = torch.empty((1, gpus, R, 512), dtype=torch.float16, device="cuda")
+    gl = torch.empty((1, gpus, R), dtype=torch.float32, device="cuda")
+    planned = mla.splitkv_plan(1, w.q_tokens, w.heads, Ls).num_splits
     rows = []
     for S in sweep:
         S = S or planned
-        po = torch.empty((1, gpus * S, w.heads, 512), dtype=torch.float16, device="cuda")
-        pl = torch.empty((1, gpus * S, w.heads), dtype=torch.float32, device="cuda")
+        po = torch.empty((1, S, R, 512), dtype=torch.float16, device="cuda")
+        pl = torch.empty((1, S, R), dtype=torch.float32, device="cuda")
         k = [0]
 
         def decode_share():
@@ -370,23 +374,30 @@ def context_parallel_share(key="b1_128k", gpus=8, n=100, sweep=(16, 32, 64, 0)):
             k[0] += 1
             c, g = i % len(shards), (i // len(shards)) % gpus
             mla.decode_splitkv(dw.q8, shards[c], tables[g], lens, dw.q_scale, dw.kv_scale,
-                               w.softmax_scale, Ls, S, 0, po[:, :S], pl[:, :S])
-        for g in range(gpus):  # every shard's slice filled once, as the all-gather would
+                               w.softmax_scale, Ls, S, 0, po, pl)
+        for g in range(gpus):  # every GPU's merged partial, as the all-gather would leave them
             mla.decode_splitkv(dw.q8, shards[0], tables[g], lens, dw.q_scale, dw.kv_scale,
-                               w.softmax_scale, Ls, S, 0, po[:, g * S:(g + 1) * S],
-                               pl[:, g * S:(g + 1) * S])
+                               w.softmax_scale, Ls, S, 0, po, pl)
+            mla.splitkv_combine_partial(po, pl, w.q_tokens, w.heads, go[:, g], gl[:, g],
+                                        gpus * R)
         dec_us = _time_fn_graph(decode_share, n)
-        comb_us = _time_fn_graph(lambda: mla.splitkv_combine(po, pl, 1, w.heads, dw.kv_scale,
-                                                             out=out, out_lse=lse), n)
+        merge_us = _time_fn_graph(lambda: mla.splitkv_combine_partial(
+            po, pl, w.q_tokens, w.heads, go[:, 0], gl[:, 0], gpus * R), n)
+        comb_us = _time_fn_graph(lambda: mla.splitkv_combine(go, gl, w.q_tokens, w.heads,
+                                                             dw.kv_scale, out=out, out_lse=lse),
+                                 n)
         rows.append({"splits_per_shard": S, "planner": S == planned,
-                     "share_decode_us": round(dec_us, 2), "combine_us": round(comb_us, 2),
-                     "all_gather_bytes_per_gpu": S * w.heads * (512 * 2 + 4)})
+                     "share_decode_us": round(dec_us, 2), "local_merge_us": round(merge_us, 2),
+                     "final_combine_us": round(comb_us, 2),
+                     "share_total_us_without_all_gather": round(dec_us + merge_us + comb_us, 2)})
         del po, pl
     del copies, shards, dw
     torch.cuda.empty_cache()
-    return {"gpus": gpus, "shard_tokens": Ls, "rows": rows,
-            "note": "decode of one GPU's shard + combine over all shards' partials; the "
-                    "all-gather of the partials between GPUs is not measured (one GPU)"}
+    return {"gpus": gpus, "shard_tokens": Ls, "all_gather_bytes_per_gpu": R * (512 * 2 + 4),
+            "rows": rows,
+            "note": "decode of one GPU's shard, merge of its splits into one partial per "
+                    "query row, final combine over all GPUs' merged partials; the all-gather "
+                    "of the merged partials between GPUs is not measured (one GPU)"}
 
 
 def step_percentiles(key, n_steps=60):

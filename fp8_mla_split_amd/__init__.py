@@ -9,6 +9,7 @@ _PUBLIC = (
     "MLAError", "Plan", "QUANTIZE_DYNAMIC_WORKSPACE_BYTES", "decode", "decode_splitkv",
     "hbm_read_probe", "kv_append_fp8_sat",
     "lib_path", "quantize_fp8_sat", "quantize_fp8_sat_dynamic", "splitkv_combine",
+    "splitkv_combine_partial",
     "splitkv_plan", "status_string",
 )
 __all__ = list(_PUBLIC)

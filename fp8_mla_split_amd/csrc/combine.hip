@@ -105,11 +105,15 @@ __device__ __forceinline__ Partial merge_entries(const Partial* red, int nw, int
 }
 
 // kBatch: load instructions a wave issues before it accumulates (kBatch * kCw splits).
-template <int kBatch>
+// kPartialOut: instead of the bf16 output, write the merged result as one partial in the
+// decode's own format (fp16 in units of the KV scale, natural-log lse) at row
+// b * out_b_stride + r, so that a further combine can merge it with others (the partials of
+// other context shards, say); out_lse is then required and v_scale unused.
+template <int kBatch, bool kPartialOut>
 __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
     const uint16_t* __restrict__ po, const float* __restrict__ pl, int S, int R, int nw,
     float v_scale, const float* __restrict__ v_scale_dev, uint16_t* __restrict__ out,
-    float* __restrict__ out_lse) {
+    float* __restrict__ out_lse, int64_t out_b_stride) {
   static_assert(kCw == 2, "the two split rows of a load sit in lanes l and l + 32");
   // all arguments in one batch of scalar loads (one trip to the argument memory)
   asm volatile("" ::"s"(po), "s"(pl), "s"(S), "s"(R), "s"(nw), "s"(v_scale), "s"(out),
@@ -188,6 +192,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
   if (lane >= kLanesPerRow) return;
   const float ws = p.ws, M = p.m;
   const float* tot = p.acc;
+  if constexpr (kPartialOut) {
+    const float f = ws > 0.f ? 1.0f / ws : 0.f;  // |O| <= 448 in units of the KV scale
+    const int64_t orow = (int64_t)b * out_b_stride + r;
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const h8 h = {(_Float16)(tot[0] * f), (_Float16)(tot[1] * f), (_Float16)(tot[2] * f),
+                  (_Float16)(tot[3] * f), (_Float16)(tot[4] * f), (_Float16)(tot[5] * f),
+                  (_Float16)(tot[6] * f), (_Float16)(tot[7] * f)};
+    *(uint4*)(out + orow * kDv + col0) = __builtin_bit_cast(uint4, h);
+    if (chunk == 0 && pos == 0) out_lse[orow] = ws > 0.f ? M + logf(ws) : -INFINITY;
+    return;
+  }
   const float f = ws > 0.f ? v_scale / ws : 0.f;
   uint4 packed;
   packed.x = (uint32_t)bf16_rne(tot[0] * f) | ((uint32_t)bf16_rne(tot[1] * f) << 16);
@@ -204,28 +219,34 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_kernel(
 template <int kBatch>
 static void launch_batch(const uint16_t* po, const float* pl, int batch, int splits, int rows,
                          float v_scale, const float* v_scale_dev, uint16_t* out, float* out_lse,
-                         hipStream_t s) {
+                         int64_t out_b_stride, bool partial_out, hipStream_t s) {
   const int64_t blocks = (int64_t)batch * rows * kCw;
   int nw = (splits + kBatch * kCw - 1) / (kBatch * kCw);
   nw = nw < 1 ? 1 : (nw > kMaxWaves ? kMaxWaves : nw);
   const size_t lds = sizeof(Partial) * kLanesPerRow * nw;
-  combine_kernel<kBatch><<<(unsigned)blocks, 64 * nw, lds, s>>>(po, pl, splits, rows, nw,
-                                                                 v_scale, v_scale_dev, out,
-                                                                 out_lse);
+  if (partial_out)
+    combine_kernel<kBatch, true><<<(unsigned)blocks, 64 * nw, lds, s>>>(
+        po, pl, splits, rows, nw, v_scale, v_scale_dev, out, out_lse, out_b_stride);
+  else
+    combine_kernel<kBatch, false><<<(unsigned)blocks, 64 * nw, lds, s>>>(
+        po, pl, splits, rows, nw, v_scale, v_scale_dev, out, out_lse, out_b_stride);
 }
 
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
                           float v_scale, const float* v_scale_dev, uint16_t* out, float* out_lse,
-                          hipStream_t s) {
+                          int64_t out_b_stride, bool partial_out, hipStream_t s) {
   // As many loads in flight per wave as there are splits to cover, up to 16; from 64 splits
   // on, 8 per wave and twice the waves (up to 16) spread the loads wider (measured on MI355X:
   // 6.2 instead of 6.5 us at 256 splits, 3.9 instead of 4.4 at 64).
   if (splits <= 4 * kCw)
-    launch_batch<4>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, s);
+    launch_batch<4>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, out_b_stride,
+                    partial_out, s);
   else if (splits <= 8 * kCw || splits >= 64)
-    launch_batch<8>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, s);
+    launch_batch<8>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, out_b_stride,
+                    partial_out, s);
   else
-    launch_batch<16>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, s);
+    launch_batch<16>(po, pl, batch, splits, rows, v_scale, v_scale_dev, out, out_lse, out_b_stride,
+                    partial_out, s);
   return hipGetLastError();
 }
 

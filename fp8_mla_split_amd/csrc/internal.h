@@ -75,9 +75,10 @@ hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t 
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int grid,
                              hipStream_t s);
 int64_t read_probe_chunk_bytes();
-// v_scale_dev: NULL, or a device float that replaces v_scale
+// v_scale_dev: NULL, or a device float that replaces v_scale.  partial_out: write fp16
+// partials (KV-scale units) + lse at rows b * out_b_stride + r instead of bf16 output.
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
                           float v_scale, const float* v_scale_dev, uint16_t* out, float* out_lse,
-                          hipStream_t s);
+                          int64_t out_b_stride, bool partial_out, hipStream_t s);
 
 }  // namespace mla

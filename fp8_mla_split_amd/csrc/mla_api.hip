@@ -251,7 +251,7 @@ mla_status combine_common(const uint16_t* partial_o_dev, const float* partial_ls
   if ((int64_t)batch * M * 2 > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
   const hipError_t e = mla::launch_combine(partial_o_dev, partial_lse_dev, batch, num_splits,
                                            (int)M, v_scale, v_scale_dev, out_bf16_dev,
-                                           out_lse_dev, (hipStream_t)stream);
+                                           out_lse_dev, M, false, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -311,6 +311,26 @@ mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* parti
                                uint16_t* out_bf16_dev, float* out_lse_dev, void* stream) {
   return combine_common(partial_o_dev, partial_lse_dev, batch, num_splits, q_tokens, heads,
                         v_scale, nullptr, out_bf16_dev, out_lse_dev, stream);
+}
+
+mla_status mla_splitkv_combine_partial(const uint16_t* partial_o_dev,
+                                       const float* partial_lse_dev, int batch, int num_splits,
+                                       int q_tokens, int heads, uint16_t* out_partial_o_dev,
+                                       float* out_partial_lse_dev, int64_t out_batch_stride_rows,
+                                       void* stream) {
+  if (batch < 0 || num_splits < 1 || q_tokens < 1 || heads < 1) return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!partial_o_dev || !partial_lse_dev || !out_partial_o_dev || !out_partial_lse_dev)
+    return MLA_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)q_tokens * heads;
+  if (M > mla::kMaxRows || num_splits > mla::kMaxSplitsCombine) return MLA_ERR_UNSUPPORTED;
+  if (out_batch_stride_rows < M) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)batch * M * 2 > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+  const hipError_t e = mla::launch_combine(partial_o_dev, partial_lse_dev, batch, num_splits,
+                                           (int)M, 1.0f, nullptr, out_partial_o_dev,
+                                           out_partial_lse_dev, out_batch_stride_rows, true,
+                                           (hipStream_t)stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 mla_status mla_splitkv_combine_dev_scale(const uint16_t* partial_o_dev,

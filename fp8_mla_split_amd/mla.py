@@ -41,6 +41,9 @@ _lib.mla_decode_splitkv_ex.restype = _i32
 _lib.mla_decode_splitkv_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                        _i32, _f32, _f32, _vp, _vp, _f32, _i32, _i32, _vp, _vp,
                                        _i64, _vp]
+_lib.mla_splitkv_combine_partial.restype = _i32
+_lib.mla_splitkv_combine_partial.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
+                                             _vp]
 _lib.mla_splitkv_combine_dev_scale.restype = _i32
 _lib.mla_splitkv_combine_dev_scale.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                                                _vp]
@@ -270,6 +273,34 @@ def splitkv_combine(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens
                                     float(v_scale), _ptr(out), _ptr(out_lse), _stream(dev)),
            "mla_splitkv_combine")
     return out, out_lse
+
+
+def splitkv_combine_partial(partial_o: torch.Tensor, partial_lse: torch.Tensor, q_tokens: int,
+                            heads: int, out_o: torch.Tensor, out_lse: torch.Tensor,
+                            out_batch_stride_rows: int = 0) -> None:
+    """Merge the S splits of each (b, row) into one partial in the decode's format (fp16 in
+    units of the KV scale, natural-log lse), written at row b * out_batch_stride_rows + r of
+    out_o / out_lse (flat row views; default stride Sq*H).  To fill slice g of a
+    [B, G, Sq*H] buffer, pass views starting at slice g and stride G*Sq*H."""
+    _dev_tensor(partial_o, torch.float16, "partial_o")
+    _dev_tensor(partial_lse, torch.float32, "partial_lse")
+    if not out_o.is_cuda or out_o.dtype != torch.float16 or not out_lse.is_cuda or \
+            out_lse.dtype != torch.float32:
+        raise ValueError("out_o must be fp16 and out_lse fp32 on the GPU")
+    B, S = partial_lse.shape[0], partial_lse.shape[1]
+    R = q_tokens * heads
+    if partial_lse.shape[2] != R or partial_o.shape[:3] != partial_lse.shape:
+        raise ValueError("partial shapes do not match [B, S, Sq*H(, 512)]")
+    stride = out_batch_stride_rows or R
+    # the rows written lie within the views given
+    last = (B - 1) * stride + R
+    if out_lse.untyped_storage().nbytes() < (out_lse.storage_offset() + last) * 4 or \
+            out_o.untyped_storage().nbytes() < (out_o.storage_offset() + last * D_V) * 2:
+        raise ValueError("out_o / out_lse are too small for the rows written")
+    _check(_lib.mla_splitkv_combine_partial(_ptr(partial_o), _ptr(partial_lse), B, S, q_tokens,
+                                            heads, _ptr(out_o), _ptr(out_lse), int(stride),
+                                            _stream(partial_o.device)),
+           "mla_splitkv_combine_partial")
 
 
 def hbm_read_probe(buf: torch.Tensor, out: torch.Tensor, grid: int) -> None:

@@ -260,6 +260,30 @@ mla_status mla_splitkv_combine(const uint16_t* partial_o_dev, const float* parti
                                uint16_t* out_bf16_dev, float* out_lse_dev, void* stream);
 
 /*
+ * The same log-sum-exp merge, with the result written as one partial in the format
+ * mla_decode_splitkv writes (fp16 bits in units of the KV scale, natural-log lse) instead of
+ * the bf16 output, so that merged results can be merged again ([A/MLA] item (2) applied in
+ * two levels).  The use it is made for: a request's KV held in contiguous shards on several
+ * GPUs (context parallel); each GPU decodes its shard and merges its own splits here into
+ * one partial row per (b, query row), the GPUs exchange those rows (Sq*H*1028 bytes per
+ * request per GPU), and mla_splitkv_combine over the G gathered partials gives the output.
+ *   partial_o_dev / partial_lse_dev   as for mla_splitkv_combine ([B, S, R, 512] / [B, S, R],
+ *                                      R = Sq * H);
+ *   out_partial_o_dev   fp16 bits; row b * out_batch_stride_rows + r receives (b, r)'s merged
+ *                       512 values;   out_partial_lse_dev  fp32, same row index;
+ *   out_batch_stride_rows  >= R: R for a [B, R] result; G * R to write slice g of a
+ *                       [B, G, R] buffer (pass the pointers offset by g * R rows).
+ * Rows whose splits are all empty get lse = -inf (and O = 0).
+ * Errors: INVALID_ARG (NULL pointers with B > 0, sizes < 1, stride < R); UNSUPPORTED
+ * (S > 4096 or Sq*H > 65536); HIP.  B == 0 enqueues nothing.
+ */
+mla_status mla_splitkv_combine_partial(const uint16_t* partial_o_dev,
+                                       const float* partial_lse_dev, int batch, int num_splits,
+                                       int q_tokens, int heads, uint16_t* out_partial_o_dev,
+                                       float* out_partial_lse_dev, int64_t out_batch_stride_rows,
+                                       void* stream);
+
+/*
  * mla_splitkv_combine with v_scale read on the device from v_scale_dev[0] (a 4-byte aligned
  * device float, finite and > 0; the KV scale the partials were computed with).  Output is
  * bit-identical to mla_splitkv_combine with the same value.  Errors as mla_splitkv_combine,

@@ -34,6 +34,7 @@ def lib():
     L.mla_decode_splitkv_dev_scales.argtypes = [v, v, v, v, i, i, i, i, i, i, v, v, f, i, i, v,
                                                 v, i64, v]
     L.mla_splitkv_combine_dev_scale.argtypes = [v, v, i, i, i, i, v, v, v, v]
+    L.mla_splitkv_combine_partial.argtypes = [v, v, i, i, i, i, v, v, i64, v]
     L.mla_decode_splitkv_ex.argtypes = [v, v, v, v, v, i, i, i, i, i, i, f, f, v, v, f, i, i, v,
                                         v, i64, v]
     L.mla_quantize_fp8_sat_dynamic.argtypes = [v, i, v, i64, v, v, i64, v]
@@ -52,7 +53,8 @@ def test_header_declares_the_entry_points():
     for n in ("mla_quantize_fp8_sat", "mla_decode_splitkv", "mla_splitkv_combine",
               "mla_splitkv_plan", "mla_status_string", "mla_quantize_fp8_sat_dynamic",
               "mla_kv_append_fp8_sat", "mla_decode_splitkv_dev_scales",
-              "mla_splitkv_combine_dev_scale", "mla_decode_splitkv_ex"):
+              "mla_splitkv_combine_dev_scale", "mla_decode_splitkv_ex",
+              "mla_splitkv_combine_partial"):
         assert n in names
 
 
@@ -212,6 +214,18 @@ def test_decode_ex_rejects_bad_arguments(lib):
     assert dec(cap=8 * 16 * 4 - 1) == WORKSPACE
     assert dec(B=0, q=None) == OK
     assert dec(B=0, q=None, ql=None) == OK
+
+
+def test_combine_partial_rejects_bad_arguments(lib):
+    c = lib.mla_splitkv_combine_partial
+    assert c(None, FAKE, 1, 4, 1, 16, FAKE, FAKE, 16, None) == INVALID
+    assert c(FAKE, None, 1, 4, 1, 16, FAKE, FAKE, 16, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, None, FAKE, 16, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, FAKE, None, 16, None) == INVALID   # lse is required
+    assert c(FAKE, FAKE, 1, 0, 1, 16, FAKE, FAKE, 16, None) == INVALID
+    assert c(FAKE, FAKE, 1, 4, 1, 16, FAKE, FAKE, 15, None) == INVALID   # stride < Sq*H
+    assert c(FAKE, FAKE, 1, 5000, 1, 16, FAKE, FAKE, 16, None) == UNSUPPORTED
+    assert c(None, None, 0, 4, 1, 16, None, None, 16, None) == OK
 
 
 def _plan(lib, B, Sq, H, L, cu, total=0):

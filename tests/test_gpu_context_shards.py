@@ -1,8 +1,10 @@
 """Context-parallel sharding of one request, shown on one GPU (runs on an MI355X).
 
 A request's KV is cut into G contiguous shards, as G GPUs would hold it; each shard is
-decoded on its own into its slice of the split-partial buffer (the slices an all-gather
-would assemble), and one combine over all G x S_local partials gives the request's output.
+decoded on its own.  Either every shard's split partials go into its slice of one partial
+buffer and one combine merges all G x S_local of them, or (what the GPUs would exchange)
+each shard first merges its own splits into one partial row per query row
+(mla_splitkv_combine_partial) and the final combine runs over the G merged partials.
 The result must meet the oracle's contract for the whole request and agree with the
 unsharded decode.  Single query token per request (every shard's positions are visible to
 it); for several query tokens only the last shard would need the causal mask.
@@ -13,7 +15,7 @@ import torch
 
 import fp8_mla_split_amd as mla
 from fp8_mla_split_amd.workload import materialize
-from synthetic import WORKLOADS
+from synthetic import WORKLOADS, Workload
 from tests.test_gpu_decode import _bf16, _compare, _oracle
 
 pytestmark = pytest.mark.gpu
@@ -61,3 +63,65 @@ def test_shards_combine_to_the_whole_request(b1, G, S_local):
     # another partition of the same sum: far inside the contract
     assert np.max(np.abs(o - _bf16(ref))) <= 2e-3
     assert np.max(np.abs(l - ref_l.cpu().numpy())) <= 1e-4
+
+
+def _two_level(dw, G, S_local, batched_stride=True):
+    """Each shard: decode, then merge its own splits into slice g of a [1, G, R] buffer (the
+    rows an all-gather over G GPUs would assemble); then the combine over the G slices."""
+    w = dw.w
+    L = int(dw.seq_lens_host[0])
+    Ls = L // G
+    shards = dw.kv_pool8[0, :L].view(G, Ls, 576)
+    R = w.heads
+    po = torch.empty((1, S_local, R, 512), dtype=torch.float16, device="cuda")
+    pl = torch.empty((1, S_local, R), dtype=torch.float32, device="cuda")
+    go = torch.full((1, G, R, 512), float("nan"), dtype=torch.float16, device="cuda")
+    gl = torch.full((1, G, R), float("nan"), dtype=torch.float32, device="cuda")
+    lens = torch.full((1,), Ls, dtype=torch.int32, device="cuda")
+    for g in range(G):
+        table = torch.full((1, 1), g, dtype=torch.int32, device="cuda")
+        mla.decode_splitkv(dw.q8, shards, table, lens, dw.q_scale, dw.kv_scale, w.softmax_scale,
+                           Ls, S_local, 0, po, pl)
+        mla.splitkv_combine_partial(po, pl, 1, R, go[:, g], gl[:, g], G * R)
+    out, lse = mla.splitkv_combine(go, gl, 1, R, dw.kv_scale)
+    torch.cuda.synchronize()
+    return _bf16(out), lse.cpu().numpy(), go, gl
+
+
+@pytest.mark.parametrize("G,S_local", [(2, 64), (8, 32), (8, 16)])
+def test_two_level_merge_matches_the_oracle(b1, G, S_local):
+    o, l, go, gl = _two_level(b1, G, S_local)
+    assert torch.isfinite(gl).all() and torch.isfinite(go.float()).all()   # every slice written
+    _compare(b1, o, l, _oracle(b1, [0]))
+    flat_o, flat_l = _sharded(b1, G, S_local)
+    assert np.max(np.abs(o - flat_o)) <= 2e-3
+    assert np.max(np.abs(l - flat_l)) <= 1e-4
+
+
+def test_partial_merge_of_a_plain_decode_equals_its_combine():
+    """Batch 3 with an output stride: the merged partial, scaled by the KV scale and rounded
+    to bf16, is the plain combine's output; its lse is the plain combine's lse."""
+    w = Workload("merge_partial", batch=3, heads=32, q_tokens=2, context=None,
+                 context_range=(1, 1), page_size=64, permuted_pool=True, seed=51)
+    dw = materialize(w, seq_lens=np.array([300, 5000, 64], np.int32))
+    po, pl, S = mla.decode_splitkv(dw.q8, dw.kv_pool8, dw.page_table, dw.seq_lens, dw.q_scale,
+                                   dw.kv_scale, w.softmax_scale, dw.max_seq_len, 7, 0)
+    R = 64
+    mo = torch.full((3, 2, R, 512), float("nan"), dtype=torch.float16, device="cuda")
+    ml = torch.full((3, 2, R), float("nan"), dtype=torch.float32, device="cuda")
+    mla.splitkv_combine_partial(po, pl, 2, 32, mo[:, 1], ml[:, 1], 2 * R)   # slice 1 of 2
+    out, lse = mla.splitkv_combine(po, pl, 2, 32, dw.kv_scale)
+    torch.cuda.synchronize()
+    assert torch.isnan(ml[:, 0]).all() and torch.isnan(mo[:, 0].float()).all()   # untouched
+    assert torch.allclose(ml[:, 1].reshape(3, 2, 32), lse, rtol=0, atol=1e-5)
+    # the plain output is the same value rounded to bf16 (half an ulp: up to 2^-8 relative,
+    # just above a power of two) where the partial holds it in fp16 (2^-11): within 2^-7
+    scaled = (mo[:, 1].float() * dw.kv_scale).reshape(3, 2, 32, 512)
+    assert torch.allclose(scaled, out.float(), rtol=2.0 ** -7, atol=1e-6)
+    # merging a single merged partial again: the same value through one more rounding
+    o2, l2 = mla.splitkv_combine(mo[:, 1:2].contiguous(), ml[:, 1:2].contiguous(), 2, 32,
+                                 dw.kv_scale)
+    torch.cuda.synchronize()
+    assert torch.allclose(o2.float(), out.float(), rtol=2.0 ** -6, atol=1e-6)
+    assert torch.equal(l2, ml[:, 1].reshape(3, 2, 32))
+    _compare(dw, _bf16(o2), l2.cpu().numpy(), _oracle(dw, [0, 1, 2]))

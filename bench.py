@@ -62,6 +62,9 @@ def _parse():
     ap.add_argument("--prep-only", action="store_true",
                     help="time only the cache-preparation entry points (KV append, quantise "
                          "with a device-derived scale) and print their JSON")
+    ap.add_argument("--cp-workload", default="",
+                    help="time only one GPU's share of a context-parallel decode of this "
+                         "workload over 8 GPUs and print its JSON")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, --steps times (the "
                          "reference kernel that calibrates HBM byte counters), then exit")
@@ -336,37 +339,44 @@ def prep_probes():
 
 
 def context_parallel_share(key="b1_128k", gpus=8, n=100, sweep=(16, 32, 64, 0)):
-    """One GPU's share of a context-parallel decode of one request, at its real shape: the
-    request's KV cut into `gpus` contiguous shards (here 16,384 of the 131,072 positions);
-    a GPU decodes its shard with S_local splits and merges them into one partial row per
-    query row (mla_splitkv_combine_partial); the GPUs would all-gather those rows (reported:
-    Sq*H*1028 bytes per GPU, not timed, it needs a second GPU) and run the final combine over
-    the `gpus` merged partials (timed).  S_local runs over `sweep` (0 = the planner's choice
-    for the shard's length).  The shard rotates over more than 512 MiB of KV so that no
-    cache holds it."""
+    """One GPU's share of a context-parallel decode, at its real shape: every request's KV
+    cut into `gpus` contiguous shards (b1_128k: 16,384 of the 131,072 positions); a GPU
+    decodes its shard with S_local splits (the shards before the last are told how many
+    positions follow them, so that only the last masks causally) and merges them into one
+    partial row per query row (mla_splitkv_combine_partial); the GPUs would all-gather those
+    rows (reported: B*Sq*H*1028 bytes per GPU, not timed, it needs a second GPU) and run the
+    final combine over the `gpus` merged partials (timed).  S_local runs over `sweep` (0 = the
+    planner's choice for the shard's length).  The shards rotate over more than 512 MiB of
+    KV so that no cache holds them."""
     import torch
     import fp8_mla_split_amd as mla
     from fp8_mla_split_amd.workload import materialize
     from synthetic import WORKLOADS
     w = WORKLOADS[key]
     dw = materialize(w)
-    L = int(dw.seq_lens_host[0])
+    B, Sq, H = w.batch, w.q_tokens, w.heads
+    L = int(dw.seq_lens_host.max())
+    assert (dw.seq_lens_host == L).all() and dw.kv_pool8.shape[1] == L and L % (32 * gpus) == 0
     Ls = L // gpus
-    R = w.q_tokens * w.heads
-    copies = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(8)]
-    shards = [c[0, :L].view(gpus, Ls, 576) for c in copies]
-    lens = torch.full((1,), Ls, dtype=torch.int32, device="cuda")
-    tables = [torch.full((1, 1), g, dtype=torch.int32, device="cuda") for g in range(gpus)]
-    out = torch.empty((1, w.q_tokens, w.heads, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((1, w.q_tokens, w.heads), dtype=torch.float32, device="cuda")
-    go = torch.empty((1, gpus, R, 512), dtype=torch.float16, device="cuda")
-    gl = torch.empty((1, gpus, R), dtype=torch.float32, device="cuda")
-    planned = mla.splitkv_plan(1, w.q_tokens, w.heads, Ls).num_splits
+    R = Sq * H
+    extra = -(-(512 << 20) // (dw.kv_pool8.numel()))
+    copies = [dw.kv_pool8] + [dw.kv_pool8.clone() for _ in range(extra)]
+    shards = [c.view(B * gpus, Ls, 576) for c in copies]          # page b * gpus + g
+    lens = torch.full((B,), Ls, dtype=torch.int32, device="cuda")
+    tables = [(torch.arange(B, dtype=torch.int32, device="cuda") * gpus + g)[:, None]
+              .contiguous() for g in range(gpus)]
+    after = [torch.full((B,), (gpus - 1 - g) * Ls, dtype=torch.int32, device="cuda")
+             if Sq > 1 else None for g in range(gpus)]
+    out = torch.empty((B, Sq, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Sq, H), dtype=torch.float32, device="cuda")
+    go = torch.empty((B, gpus, R, 512), dtype=torch.float16, device="cuda")
+    gl = torch.empty((B, gpus, R), dtype=torch.float32, device="cuda")
+    planned = mla.splitkv_plan(B, Sq, H, Ls).num_splits
     rows = []
     for S in sweep:
         S = S or planned
-        po = torch.empty((1, S, R, 512), dtype=torch.float16, device="cuda")
-        pl = torch.empty((1, S, R), dtype=torch.float32, device="cuda")
+        po = torch.empty((B, S, R, 512), dtype=torch.float16, device="cuda")
+        pl = torch.empty((B, S, R), dtype=torch.float32, device="cuda")
         k = [0]
 
         def decode_share():
@@ -374,18 +384,17 @@ def context_parallel_share(key="b1_128k", gpus=8, n=100, sweep=(16, 32, 64, 0)):
             k[0] += 1
             c, g = i % len(shards), (i // len(shards)) % gpus
             mla.decode_splitkv(dw.q8, shards[c], tables[g], lens, dw.q_scale, dw.kv_scale,
-                               w.softmax_scale, Ls, S, 0, po, pl)
+                               w.softmax_scale, Ls, S, 0, po, pl, ctx_after=after[g])
         for g in range(gpus):  # every GPU's merged partial, as the all-gather would leave them
             mla.decode_splitkv(dw.q8, shards[0], tables[g], lens, dw.q_scale, dw.kv_scale,
-                               w.softmax_scale, Ls, S, 0, po, pl)
-            mla.splitkv_combine_partial(po, pl, w.q_tokens, w.heads, go[:, g], gl[:, g],
-                                        gpus * R)
-        dec_us = _time_fn_graph(decode_share, n)
+                               w.softmax_scale, Ls, S, 0, po, pl, ctx_after=after[g])
+            mla.splitkv_combine_partial(po, pl, Sq, H, go[:, g], gl[:, g], gpus * R)
+        reps = n if B * Ls <= (1 << 17) else 5
+        dec_us = _time_fn_graph(decode_share, reps)
         merge_us = _time_fn_graph(lambda: mla.splitkv_combine_partial(
-            po, pl, w.q_tokens, w.heads, go[:, 0], gl[:, 0], gpus * R), n)
-        comb_us = _time_fn_graph(lambda: mla.splitkv_combine(go, gl, w.q_tokens, w.heads,
-                                                             dw.kv_scale, out=out, out_lse=lse),
-                                 n)
+            po, pl, Sq, H, go[:, 0], gl[:, 0], gpus * R), n)
+        comb_us = _time_fn_graph(lambda: mla.splitkv_combine(go, gl, Sq, H, dw.kv_scale,
+                                                             out=out, out_lse=lse), n)
         rows.append({"splits_per_shard": S, "planner": S == planned,
                      "share_decode_us": round(dec_us, 2), "local_merge_us": round(merge_us, 2),
                      "final_combine_us": round(comb_us, 2),
@@ -393,8 +402,8 @@ def context_parallel_share(key="b1_128k", gpus=8, n=100, sweep=(16, 32, 64, 0)):
         del po, pl
     del copies, shards, dw
     torch.cuda.empty_cache()
-    return {"gpus": gpus, "shard_tokens": Ls, "all_gather_bytes_per_gpu": R * (512 * 2 + 4),
-            "rows": rows,
+    return {"workload": w.name, "gpus": gpus, "shard_tokens": Ls,
+            "all_gather_bytes_per_gpu": B * R * (512 * 2 + 4), "rows": rows,
             "note": "decode of one GPU's shard, merge of its splits into one partial per "
                     "query row, final combine over all GPUs' merged partials; the all-gather "
                     "of the merged partials between GPUs is not measured (one GPU)"}
@@ -568,6 +577,11 @@ def main():
     sys.path.insert(0, ROOT)
     if a.prep_only:
         print(json.dumps({"cache_prep": prep_probes()}), flush=True)
+        return
+    if a.cp_workload:
+        print(json.dumps({"context_parallel_share": context_parallel_share(
+            a.cp_workload, sweep=(0,) if a.cp_workload != "b1_128k" else (16, 32, 64, 0))}),
+            flush=True)
         return
     t_wall = time.time()
     q_lens = [int(x) for x in a.q_lens.split(",")] if a.q_lens else None

@@ -338,12 +338,17 @@ void decode_kernel(const DecodeParams p) {
   const int pt_hint = ptrow[(uint32_t)min((int)fast_div((uint32_t)(s * p.tiles_hint), p.div_tpp),
                                           p.max_pages - 1)];
   int L = seq_lens[b];
-  // query tokens of this request: all q_tokens, or its own count when requests differ
-  int qlen = p.q_tokens;
+  // query tokens of this request: all q_tokens, or its own count when requests differ; and
+  // the request's context positions after the ones this call sees (a context shard other
+  // than the last: the query tokens are the context's last positions, so every position
+  // here is visible once that count reaches the query count)
+  int qlen = p.q_tokens, after = 0;
   if constexpr (kRagged) {
-    qlen = ((const __attribute__((address_space(4))) int32_t*)p.q_lens)[b];
-    asm volatile("" ::"s"(L), "s"(pt_hint), "s"(qlen));  // all three loads go out together
+    if (p.q_lens) qlen = ((const __attribute__((address_space(4))) int32_t*)p.q_lens)[b];
+    if (p.ctx_after) after = ((const __attribute__((address_space(4))) int32_t*)p.ctx_after)[b];
+    asm volatile("" ::"s"(L), "s"(pt_hint), "s"(qlen), "s"(after));  // all out together
     qlen = qlen < 0 ? 0 : (qlen > p.q_tokens ? p.q_tokens : qlen);
+    after = after < 0 ? 0 : (after > p.q_tokens ? p.q_tokens : after);
   } else {
     asm volatile("" ::"s"(L), "s"(pt_hint));  // both loads go out before either is waited for
   }
@@ -523,9 +528,9 @@ void decode_kernel(const DecodeParams p) {
   // A row whose query token t is past its request's count sees nothing (lim = -1), like a
   // query with no visible position: its lse is -inf.
   const int t_r = (int)fast_div((uint32_t)R, p.div_heads);
-  const int lim_r = kRagged ? (t_r < qlen ? L - qlen + t_r : -1) : L - qlen + t_r;
+  const int lim_r = kRagged ? (t_r < qlen ? L + after - qlen + t_r : -1) : L - qlen + t_r;
   const int lim = row_ok ? lim_r : 0x7FFFFFFF;
-  int lim_min = L - qlen + (int)fast_div((uint32_t)wrow0, p.div_heads);
+  int lim_min = L + after - qlen + (int)fast_div((uint32_t)wrow0, p.div_heads);
   if constexpr (kRagged) {  // the wave's smallest limit is -1 if it holds an absent row
     const int t_hi = (int)fast_div((uint32_t)min(wrow0 + 31, M - 1), p.div_heads);
     if (t_hi >= qlen) lim_min = -1;
@@ -934,7 +939,8 @@ hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t 
   const int64_t blocks = ((units + 7) / 8) * 8 * p.groups;
   // an even number of tiles per page (and pages under 4 GiB) takes the paired-tile cursor
   const bool paired = (p.page_size / kTile) % 2 == 0 && p.page_bytes < (int64_t(1) << 32);
-  const int v = (paired ? 1 : 0) | (p.q_scale_dev != nullptr ? 2 : 0) | (p.q_lens ? 4 : 0);
+  const int v = (paired ? 1 : 0) | (p.q_scale_dev != nullptr ? 2 : 0) |
+                (p.q_lens || p.ctx_after ? 4 : 0);
   const dim3 grid((unsigned)blocks), block(256);
   switch (v) {
     case 0: decode_kernel<false, false, false><<<grid, block, 0, s>>>(p); break;

@@ -57,6 +57,9 @@ struct DecodeParams {
   // per-request query-token counts (NULL: every request has q_tokens); device values are
   // clamped to [0, q_tokens]
   const int32_t* q_lens;
+  // per-request count of context positions after the ones this call sees (NULL: none); device
+  // values are clamped to [0, q_tokens], which already makes every position visible
+  const int32_t* ctx_after;
 };
 
 // c2 from the three scales: products in double, one rounding to float (host and device alike)

@@ -160,7 +160,7 @@ namespace {
 // count for all requests (q_lens_dev == NULL) or one per request.
 mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                          const int32_t* page_table_dev, const int32_t* seq_lens_dev,
-                         const int32_t* q_lens_dev, int batch,
+                         const int32_t* q_lens_dev, const int32_t* ctx_after_dev, int batch,
                          int q_tokens, int heads, int page_size, int max_pages, int max_seq_len,
                          float q_scale, float kv_scale, const float* q_scale_dev,
                          const float* kv_scale_dev, float softmax_scale, int num_splits,
@@ -179,10 +179,11 @@ mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   if (dev && (kv_scale_dev == nullptr || ((uintptr_t)q_scale_dev & 3) != 0 ||
               ((uintptr_t)kv_scale_dev & 3) != 0))
     return MLA_ERR_INVALID_ARG;
-  if (((uintptr_t)q_lens_dev & 3) != 0) return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)q_lens_dev & 3) != 0 || ((uintptr_t)ctx_after_dev & 3) != 0)
+    return MLA_ERR_INVALID_ARG;
   const int64_t M = (int64_t)q_tokens * heads;
   if (M > mla::kMaxRows || page_size % mla::kTile != 0 ||
-      (int64_t)max_pages * page_size > 0x7FFFFFFFLL - 64)
+      (int64_t)max_pages * page_size + 2LL * q_tokens > 0x7FFFFFFFLL - 64)
     return MLA_ERR_UNSUPPORTED;
   if (rows_per_group != 0 && rows_per_group != 128) return MLA_ERR_UNSUPPORTED;
   int S = num_splits, r = rows_per_group;
@@ -233,6 +234,7 @@ mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   p.kv_scale_dev = kv_scale_dev;
   p.softmax_scale = softmax_scale;
   p.q_lens = q_lens_dev;
+  p.ctx_after = ctx_after_dev;
   const hipError_t e = mla::launch_decode(p, r, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -266,7 +268,8 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                               int num_splits, int rows_per_group, uint16_t* partial_o_dev,
                               float* partial_lse_dev, int64_t partial_rows_capacity,
                               void* stream) {
-  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, nullptr, batch,
+  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, nullptr, nullptr,
+                       batch,
                        q_tokens, heads, page_size, max_pages, max_seq_len, q_scale, kv_scale,
                        nullptr, nullptr,
                        softmax_scale, num_splits, rows_per_group, partial_o_dev, partial_lse_dev,
@@ -283,7 +286,8 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
                                          uint16_t* partial_o_dev, float* partial_lse_dev,
                                          int64_t partial_rows_capacity, void* stream) {
   if (q_scale_dev == nullptr || kv_scale_dev == nullptr) return MLA_ERR_INVALID_ARG;
-  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, nullptr, batch,
+  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, nullptr, nullptr,
+                       batch,
                        q_tokens, heads, page_size, max_pages, max_seq_len, 1.0f, 1.0f,
                        q_scale_dev, kv_scale_dev,
                        softmax_scale, num_splits, rows_per_group, partial_o_dev, partial_lse_dev,
@@ -292,7 +296,8 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
 
 mla_status mla_decode_splitkv_ex(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                                  const int32_t* page_table_dev, const int32_t* seq_lens_dev,
-                                 const int32_t* q_lens_dev, int batch, int q_tokens, int heads,
+                                 const int32_t* q_lens_dev, const int32_t* ctx_after_dev,
+                                 int batch, int q_tokens, int heads,
                                  int page_size, int max_pages, int max_seq_len, float q_scale,
                                  float kv_scale, const float* q_scale_dev,
                                  const float* kv_scale_dev, float softmax_scale, int num_splits,
@@ -300,7 +305,8 @@ mla_status mla_decode_splitkv_ex(const uint8_t* q8_dev, const uint8_t* kv_pool_d
                                  float* partial_lse_dev, int64_t partial_rows_capacity,
                                  void* stream) {
   if ((q_scale_dev == nullptr) != (kv_scale_dev == nullptr)) return MLA_ERR_INVALID_ARG;
-  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, q_lens_dev, batch,
+  return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, q_lens_dev,
+                       ctx_after_dev, batch,
                        q_tokens, heads, page_size, max_pages, max_seq_len, q_scale, kv_scale,
                        q_scale_dev, kv_scale_dev, softmax_scale, num_splits, rows_per_group,
                        partial_o_dev, partial_lse_dev, partial_rows_capacity, stream);

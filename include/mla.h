@@ -225,6 +225,15 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
  *                0 .. L_b - q_lens_dev[b] + t.  Rows of slots t >= q_lens_dev[b] see nothing:
  *                their partial lse is -inf in every split, so the combine gives O = 0 and
  *                lse = -inf for them.  NULL: every request has q_tokens tokens.
+ *   ctx_after_dev int32 [B] (device) or NULL.  The number of request b's context positions
+ *                that come after the L_b positions this call reads (device values clamped to
+ *                [0, q_tokens]; 0 = none).  For a request whose KV is split into
+ *                contiguous shards (on several GPUs, say): the query tokens are the last
+ *                positions of the whole context, so position n of this shard is visible to
+ *                token t when n <= L_b + ctx_after[b] - q_lens[b] + t; with ctx_after[b] >=
+ *                q_lens[b] every position of the shard is visible.  Each shard's partials
+ *                (merged by mla_splitkv_combine_partial) then combine into the request's
+ *                output.  NULL: the call sees the end of every request's context.
  *   q_scale_dev, kv_scale_dev  both NULL (q_scale and kv_scale are used) or both device
  *                floats (as mla_decode_splitkv_dev_scales).
  * Errors as mla_decode_splitkv, plus INVALID_ARG for exactly one NULL scale pointer or a
@@ -232,7 +241,8 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
  */
 mla_status mla_decode_splitkv_ex(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                                  const int32_t* page_table_dev, const int32_t* seq_lens_dev,
-                                 const int32_t* q_lens_dev, int batch, int q_tokens, int heads,
+                                 const int32_t* q_lens_dev, const int32_t* ctx_after_dev,
+                                 int batch, int q_tokens, int heads,
                                  int page_size, int max_pages, int max_seq_len, float q_scale,
                                  float kv_scale, const float* q_scale_dev,
                                  const float* kv_scale_dev, float softmax_scale, int num_splits,

@@ -6,8 +6,8 @@ buffer and one combine merges all G x S_local of them, or (what the GPUs would e
 each shard first merges its own splits into one partial row per query row
 (mla_splitkv_combine_partial) and the final combine runs over the G merged partials.
 The result must meet the oracle's contract for the whole request and agree with the
-unsharded decode.  Single query token per request (every shard's positions are visible to
-it); for several query tokens only the last shard would need the causal mask.
+unsharded decode.  With several query tokens, the shards other than the last are told how
+many context positions follow them (ctx_after), so that only the last one masks.
 """
 import numpy as np
 import pytest
@@ -16,6 +16,7 @@ import torch
 import fp8_mla_split_amd as mla
 from fp8_mla_split_amd.workload import materialize
 from synthetic import WORKLOADS, Workload
+from tests import oracle_side as ors
 from tests.test_gpu_decode import _bf16, _compare, _oracle
 
 pytestmark = pytest.mark.gpu
@@ -125,3 +126,44 @@ def test_partial_merge_of_a_plain_decode_equals_its_combine():
     assert torch.allclose(o2.float(), out.float(), rtol=2.0 ** -6, atol=1e-6)
     assert torch.equal(l2, ml[:, 1].reshape(3, 2, 32))
     _compare(dw, _bf16(o2), l2.cpu().numpy(), _oracle(dw, [0, 1, 2]))
+
+
+@pytest.mark.parametrize("q_lens", [None, [8, 3]])
+def test_shards_with_several_query_tokens(q_lens):
+    """Verify shape (8 query tokens, causal among them) over 3 context shards per request:
+    the shards other than the last are told how many positions follow them (ctx_after), so
+    all their positions are visible; the last shard masks as usual.  Each shard's splits are
+    merged into its slice, and the combine over the slices meets the oracle's contract for
+    the whole requests (optionally with per-request draft counts)."""
+    G, Ls, B, Sq, H = 3, 1024, 2, 8, 32
+    w = Workload("cp_verify", batch=B, heads=H, q_tokens=Sq, context=G * Ls, seed=61)
+    dw = materialize(w)
+    R = Sq * H
+    shards = dw.kv_pool8[:, :G * Ls].reshape(B * G, Ls, 576)   # page b * G + g
+    po = torch.empty((B, 4, R, 512), dtype=torch.float16, device="cuda")
+    pl = torch.empty((B, 4, R), dtype=torch.float32, device="cuda")
+    go = torch.full((B, G, R, 512), float("nan"), dtype=torch.float16, device="cuda")
+    gl = torch.full((B, G, R), float("nan"), dtype=torch.float32, device="cuda")
+    lens = torch.full((B,), Ls, dtype=torch.int32, device="cuda")
+    ql = None if q_lens is None else torch.tensor(q_lens, dtype=torch.int32, device="cuda")
+    for g in range(G):
+        table = (torch.arange(B, dtype=torch.int32, device="cuda") * G + g)[:, None].contiguous()
+        after = torch.full((B,), (G - 1 - g) * Ls, dtype=torch.int32, device="cuda")
+        mla.decode_splitkv(dw.q8, shards, table, lens, dw.q_scale, dw.kv_scale,
+                           w.softmax_scale, Ls, 4, 0, po, pl, q_lens=ql, ctx_after=after)
+        mla.splitkv_combine_partial(po, pl, Sq, H, go[:, g], gl[:, g], G * R)
+    out, lse = mla.splitkv_combine(go, gl, Sq, H, dw.kv_scale)
+    torch.cuda.synchronize()
+    o, l = _bf16(out), lse.cpu().numpy()
+    if q_lens is None:
+        _compare(dw, o, l, _oracle(dw, range(B)))
+        return
+    q_scale, kv_scale = ors.scales(w, dw.seq_lens_host)
+    for b in range(B):
+        L = int(dw.seq_lens_host[b])
+        ref_o, ref_l = ors.attention_request(w, b, L, ors.q8_request(w, b, q_scale), q_scale,
+                                             ors.kv8_request(w, b, L, kv_scale), kv_scale,
+                                             q_len=q_lens[b])
+        k = q_lens[b]
+        assert np.all(o[b][k:] == 0) and np.all(l[b][k:] == -np.inf)
+        ors.check_output(o[b][:k], ref_o[:k], l[b][:k], ref_l[:k])

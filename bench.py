@@ -48,6 +48,9 @@ def _parse():
     ap.add_argument("--also", default="b16_128k",
                     help="second workload reported alongside ('' = none)")
     ap.add_argument("--splits", type=int, default=0, help="0 = planner")
+    ap.add_argument("--order", choices=("request", "longest"), default="request",
+                    help="dispatch order of the requests' workgroups (longest first balances "
+                         "mixed lengths)")
     ap.add_argument("--q-lens", default="",
                     help="comma-separated query-token count per request (verify step with a "
                          "different number of draft tokens per request); empty = all q_tokens")
@@ -100,7 +103,7 @@ def _time_graph(g, reps):
 
 
 def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_bytes=512 << 20,
-                 dev_scales=False, q_lens=None):
+                 dev_scales=False, q_lens=None, longest_first=False):
     """One decode step = Q quantise + split-KV decode + combine, timed over `steps` steps.
     dev_scales: Q's scale is derived on the device (mla_quantize_fp8_sat_dynamic) and the
     decode and combine read both scales from device memory."""
@@ -143,9 +146,15 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
             raise SystemExit(f"--q-lens needs {B} counts for {w.name}")
         ql = torch.tensor(q_lens, dtype=torch.int32, device="cuda")
 
+    order = None
+    if longest_first:  # the caller knows the lengths: longest requests dispatched first
+        order = torch.from_numpy(np.argsort(-dw.seq_lens_host, kind="stable")
+                                 .astype(np.int32)).cuda()
+
     def decode(i):
         mla.decode_splitkv(q8, pools[i % copies], dw.page_table, dw.seq_lens, q_scale,
-                           kv_scale, w.softmax_scale, dw.max_seq_len, S, r, po, pl, q_lens=ql)
+                           kv_scale, w.softmax_scale, dw.max_seq_len, S, r, po, pl, q_lens=ql,
+                           order=order)
 
     def combine():
         mla.splitkv_combine(po, pl, Sq, H, kv_scale, out=out, out_lse=lse)
@@ -165,6 +174,8 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
            "scales": "device (Q amax on the GPU)" if dev_scales else "host"}
     if q_lens:
         res["q_lens"] = list(q_lens)
+    if longest_first:
+        res["order"] = "longest first"
     if eager:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         t0 = torch.cuda.Event(enable_timing=True)
@@ -586,7 +597,7 @@ def main():
     t_wall = time.time()
     q_lens = [int(x) for x in a.q_lens.split(",")] if a.q_lens else None
     main_res = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager,
-                            q_lens=q_lens)
+                            q_lens=q_lens, longest_first=a.order == "longest")
     print(f"[bench] {a.workload}: {main_res['us_per_step']:.2f} us/step (decode "
           f"{main_res['decode_us']:.2f} us, {main_res['decode_gbps']:.0f} GB/s; combine "
           f"{main_res['combine_us']:.2f} us; Q quantize {main_res['quantize_q_us']:.2f} us)",
@@ -642,8 +653,8 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/KV, per-tensor scales)",
         "config": {k: main_res[k] for k in ("workload", "batch", "heads", "q_tokens", "context",
                                             "num_splits", "rows_per_group", "kv_copies",
-                                            "timing")} | (
-            {"q_lens": main_res["q_lens"]} if "q_lens" in main_res else {}),
+                                            "timing")} | {
+            k: main_res[k] for k in ("q_lens", "order") if k in main_res},
         "kv_read_gbps_step": round(main_res["step_kv_gbps"], 1),
         "kv_read_pct_of_peak_step": round(100 * main_res["step_kv_gbps"] / HBM_PEAK_GBPS, 2),
         "breakdown_us": {k: round(main_res[k], 3) for k in ("quantize_q_us", "decode_us",

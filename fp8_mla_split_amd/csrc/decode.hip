@@ -308,7 +308,16 @@ void decode_kernel(const DecodeParams p) {
   const int g = kx - kxg * G;
   const int u = kxg * 8 + (id & 7);
   if (u >= p.batch * S) return;
-  const int b = (int)fast_div((uint32_t)u, p.div_splits), s = u - b * S;
+  const int b_slot = (int)fast_div((uint32_t)u, p.div_splits), s = u - b_slot * S;
+  // the request of this slot: slots are dispatched in order, so an order that puts the
+  // longest requests first balances the CUs when lengths differ (values clamped into range)
+  int b = b_slot;
+  if constexpr (kRagged) {
+    if (p.order) {
+      b = ((const __attribute__((address_space(4))) int32_t*)p.order)[b_slot];
+      b = b < 0 ? 0 : (b >= p.batch ? p.batch - 1 : b);
+    }
+  }
 
   // Wave-uniform scalars come from the constant address space (scalar loads, lgkmcnt).
   const __attribute__((address_space(4))) int32_t* seq_lens =
@@ -940,7 +949,7 @@ hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t 
   // an even number of tiles per page (and pages under 4 GiB) takes the paired-tile cursor
   const bool paired = (p.page_size / kTile) % 2 == 0 && p.page_bytes < (int64_t(1) << 32);
   const int v = (paired ? 1 : 0) | (p.q_scale_dev != nullptr ? 2 : 0) |
-                (p.q_lens || p.ctx_after ? 4 : 0);
+                (p.q_lens || p.ctx_after || p.order ? 4 : 0);
   const dim3 grid((unsigned)blocks), block(256);
   switch (v) {
     case 0: decode_kernel<false, false, false><<<grid, block, 0, s>>>(p); break;

@@ -60,6 +60,9 @@ struct DecodeParams {
   // per-request count of context positions after the ones this call sees (NULL: none); device
   // values are clamped to [0, q_tokens], which already makes every position visible
   const int32_t* ctx_after;
+  // the order in which requests' workgroups are dispatched (a permutation of [0, B); NULL:
+  // request order)
+  const int32_t* order;
 };
 
 // c2 from the three scales: products in double, one rounding to float (host and device alike)

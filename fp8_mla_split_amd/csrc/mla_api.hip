@@ -160,7 +160,8 @@ namespace {
 // count for all requests (q_lens_dev == NULL) or one per request.
 mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                          const int32_t* page_table_dev, const int32_t* seq_lens_dev,
-                         const int32_t* q_lens_dev, const int32_t* ctx_after_dev, int batch,
+                         const int32_t* q_lens_dev, const int32_t* ctx_after_dev,
+                         const int32_t* order_dev, int batch,
                          int q_tokens, int heads, int page_size, int max_pages, int max_seq_len,
                          float q_scale, float kv_scale, const float* q_scale_dev,
                          const float* kv_scale_dev, float softmax_scale, int num_splits,
@@ -179,7 +180,8 @@ mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   if (dev && (kv_scale_dev == nullptr || ((uintptr_t)q_scale_dev & 3) != 0 ||
               ((uintptr_t)kv_scale_dev & 3) != 0))
     return MLA_ERR_INVALID_ARG;
-  if (((uintptr_t)q_lens_dev & 3) != 0 || ((uintptr_t)ctx_after_dev & 3) != 0)
+  if (((uintptr_t)q_lens_dev & 3) != 0 || ((uintptr_t)ctx_after_dev & 3) != 0 ||
+      ((uintptr_t)order_dev & 3) != 0)
     return MLA_ERR_INVALID_ARG;
   const int64_t M = (int64_t)q_tokens * heads;
   if (M > mla::kMaxRows || page_size % mla::kTile != 0 ||
@@ -235,6 +237,7 @@ mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   p.softmax_scale = softmax_scale;
   p.q_lens = q_lens_dev;
   p.ctx_after = ctx_after_dev;
+  p.order = order_dev;
   const hipError_t e = mla::launch_decode(p, r, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
@@ -269,7 +272,7 @@ mla_status mla_decode_splitkv(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                               float* partial_lse_dev, int64_t partial_rows_capacity,
                               void* stream) {
   return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, nullptr, nullptr,
-                       batch,
+                       nullptr, batch,
                        q_tokens, heads, page_size, max_pages, max_seq_len, q_scale, kv_scale,
                        nullptr, nullptr,
                        softmax_scale, num_splits, rows_per_group, partial_o_dev, partial_lse_dev,
@@ -287,7 +290,7 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
                                          int64_t partial_rows_capacity, void* stream) {
   if (q_scale_dev == nullptr || kv_scale_dev == nullptr) return MLA_ERR_INVALID_ARG;
   return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, nullptr, nullptr,
-                       batch,
+                       nullptr, batch,
                        q_tokens, heads, page_size, max_pages, max_seq_len, 1.0f, 1.0f,
                        q_scale_dev, kv_scale_dev,
                        softmax_scale, num_splits, rows_per_group, partial_o_dev, partial_lse_dev,
@@ -297,7 +300,7 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
 mla_status mla_decode_splitkv_ex(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                                  const int32_t* page_table_dev, const int32_t* seq_lens_dev,
                                  const int32_t* q_lens_dev, const int32_t* ctx_after_dev,
-                                 int batch, int q_tokens, int heads,
+                                 const int32_t* order_dev, int batch, int q_tokens, int heads,
                                  int page_size, int max_pages, int max_seq_len, float q_scale,
                                  float kv_scale, const float* q_scale_dev,
                                  const float* kv_scale_dev, float softmax_scale, int num_splits,
@@ -306,7 +309,7 @@ mla_status mla_decode_splitkv_ex(const uint8_t* q8_dev, const uint8_t* kv_pool_d
                                  void* stream) {
   if ((q_scale_dev == nullptr) != (kv_scale_dev == nullptr)) return MLA_ERR_INVALID_ARG;
   return decode_common(q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, q_lens_dev,
-                       ctx_after_dev, batch,
+                       ctx_after_dev, order_dev, batch,
                        q_tokens, heads, page_size, max_pages, max_seq_len, q_scale, kv_scale,
                        q_scale_dev, kv_scale_dev, softmax_scale, num_splits, rows_per_group,
                        partial_o_dev, partial_lse_dev, partial_rows_capacity, stream);

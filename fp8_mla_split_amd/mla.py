@@ -38,9 +38,9 @@ _lib.mla_decode_splitkv_dev_scales.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _
                                                _i32, _vp, _vp, _f32, _i32, _i32, _vp, _vp, _i64,
                                                _vp]
 _lib.mla_decode_splitkv_ex.restype = _i32
-_lib.mla_decode_splitkv_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                       _i32, _i32, _f32, _f32, _vp, _vp, _f32, _i32, _i32, _vp,
-                                       _vp, _i64, _vp]
+_lib.mla_decode_splitkv_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _f32, _f32, _vp, _vp, _f32, _i32, _i32,
+                                       _vp, _vp, _i64, _vp]
 _lib.mla_splitkv_combine_partial.restype = _i32
 _lib.mla_splitkv_combine_partial.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
                                              _vp]
@@ -183,14 +183,16 @@ def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.T
                    rows_per_group: int = 0, partial_o: Optional[torch.Tensor] = None,
                    partial_lse: Optional[torch.Tensor] = None,
                    q_lens: Optional[torch.Tensor] = None,
-                   ctx_after: Optional[torch.Tensor] = None):
+                   ctx_after: Optional[torch.Tensor] = None,
+                   order: Optional[torch.Tensor] = None):
     """Split-KV partial attention.  Returns ``(partial_o, partial_lse, num_splits)``.
     q_scale and kv_scale are host numbers, or both 1-element fp32 device tensors (e.g. from
     quantize_fp8_sat_dynamic), which selects mla_decode_splitkv_dev_scales.  q_lens (int32
     [B] on the GPU) gives each request its own number of query tokens (<= Sq; the first
     q_lens[b] slots of q8[b]), through mla_decode_splitkv_ex; ctx_after (int32 [B] on the GPU)
     counts each request's context positions after the ones this call reads (a context shard
-    other than the last).
+    other than the last); order (int32 [B] on the GPU, a permutation) is the order in which
+    requests' workgroups are dispatched, longest first for mixed lengths.
 
     q8 [B, Sq, H, 576] uint8; kv_pool8 [pages, page_size, 576] uint8; page_table
     [B, max_pages] int32; seq_lens [B] int32.  partial_o [B, S, Sq*H, 512] fp16 (in units of
@@ -220,15 +222,15 @@ def decode_splitkv(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.T
     dq, dk = _dev_scale(q_scale, "q_scale"), _dev_scale(kv_scale, "kv_scale")
     if dq != dk:
         raise ValueError("q_scale and kv_scale must both be host numbers or both device tensors")
-    if q_lens is not None or ctx_after is not None:
-        for t, name in ((q_lens, "q_lens"), (ctx_after, "ctx_after")):
+    if q_lens is not None or ctx_after is not None or order is not None:
+        for t, name in ((q_lens, "q_lens"), (ctx_after, "ctx_after"), (order, "order")):
             if t is not None:
                 _dev_tensor(t, torch.int32, name)
                 if t.numel() != B:
                     raise ValueError(f"{name} must hold one count per request")
         _check(_lib.mla_decode_splitkv_ex(
             _ptr(q8), _ptr(kv_pool8), _ptr(page_table), _ptr(seq_lens), _ptr(q_lens),
-            _ptr(ctx_after), B, Sq, H,
+            _ptr(ctx_after), _ptr(order), B, Sq, H,
             page_size, page_table.shape[1], max_seq_len, 1.0 if dq else float(q_scale),
             1.0 if dk else float(kv_scale), _ptr(q_scale) if dq else None,
             _ptr(kv_scale) if dk else None, float(softmax_scale), num_splits, rows_per_group,

@@ -234,6 +234,14 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
  *                q_lens[b] every position of the shard is visible.  Each shard's partials
  *                (merged by mla_splitkv_combine_partial) then combine into the request's
  *                output.  NULL: the call sees the end of every request's context.
+ *   order_dev    int32 [B] (device) or NULL.  A permutation of the requests: the workgroups
+ *                of request order_dev[0] are dispatched first, then those of order_dev[1],
+ *                and so on.  Every request's chunk size follows its own length, so when
+ *                lengths differ, putting the longest requests first (the caller knows the
+ *                lengths) keeps the last-dispatched workgroups short and the CUs evenly
+ *                loaded.  The result does not depend on it.  Values are clamped into
+ *                [0, B); an order that is not a permutation computes some requests twice
+ *                and leaves others unwritten.  NULL: request order.
  *   q_scale_dev, kv_scale_dev  both NULL (q_scale and kv_scale are used) or both device
  *                floats (as mla_decode_splitkv_dev_scales).
  * Errors as mla_decode_splitkv, plus INVALID_ARG for exactly one NULL scale pointer or a
@@ -242,7 +250,7 @@ mla_status mla_decode_splitkv_dev_scales(const uint8_t* q8_dev, const uint8_t* k
 mla_status mla_decode_splitkv_ex(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                                  const int32_t* page_table_dev, const int32_t* seq_lens_dev,
                                  const int32_t* q_lens_dev, const int32_t* ctx_after_dev,
-                                 int batch, int q_tokens, int heads,
+                                 const int32_t* order_dev, int batch, int q_tokens, int heads,
                                  int page_size, int max_pages, int max_seq_len, float q_scale,
                                  float kv_scale, const float* q_scale_dev,
                                  const float* kv_scale_dev, float softmax_scale, int num_splits,

@@ -35,8 +35,8 @@ def lib():
                                                 v, i64, v]
     L.mla_splitkv_combine_dev_scale.argtypes = [v, v, i, i, i, i, v, v, v, v]
     L.mla_splitkv_combine_partial.argtypes = [v, v, i, i, i, i, v, v, i64, v]
-    L.mla_decode_splitkv_ex.argtypes = [v, v, v, v, v, v, i, i, i, i, i, i, f, f, v, v, f, i, i,
-                                        v, v, i64, v]
+    L.mla_decode_splitkv_ex.argtypes = [v, v, v, v, v, v, v, i, i, i, i, i, i, f, f, v, v, f, i,
+                                        i, v, v, i64, v]
     L.mla_quantize_fp8_sat_dynamic.argtypes = [v, i, v, i64, v, v, i64, v]
     L.mla_kv_append_fp8_sat.argtypes = [v, v, i64, v, v, i, i, i, i, f, v]
     return L
@@ -197,15 +197,16 @@ def test_dev_scale_variants_reject_bad_arguments(lib):
 def test_decode_ex_rejects_bad_arguments(lib):
     d = lib.mla_decode_splitkv_ex
 
-    def dec(ql=FAKE, ca=None, qsd=None, ksd=None, qs=1.0, ks=1.0, **kw):
+    def dec(ql=FAKE, ca=None, od=None, qsd=None, ksd=None, qs=1.0, ks=1.0, **kw):
         a = dict(q=FAKE, B=1, P=64, cap=1 << 20, Sq=8)
         a.update(kw)
-        return d(a["q"], FAKE, FAKE, FAKE, ql, ca, a["B"], a["Sq"], 16, a["P"], 4, 256, qs, ks,
-                 qsd, ksd, 0.07, 4, 128, FAKE, FAKE, a["cap"], None)
+        return d(a["q"], FAKE, FAKE, FAKE, ql, ca, od, a["B"], a["Sq"], 16, a["P"], 4, 256, qs,
+                 ks, qsd, ksd, 0.07, 4, 128, FAKE, FAKE, a["cap"], None)
     assert dec(qsd=FAKE) == INVALID                     # one scale pointer without the other
     assert dec(ksd=FAKE) == INVALID
     assert dec(ql=ctypes.c_void_p(0x1002)) == INVALID   # q_lens misaligned
     assert dec(ca=ctypes.c_void_p(0x1001)) == INVALID   # ctx_after misaligned
+    assert dec(od=ctypes.c_void_p(0x1003)) == INVALID   # order misaligned
     assert dec(qs=0.0) == INVALID                       # host scales checked when used
     # with device scales the host values are not used: the call gets as far as the
     # workspace check (which fails here, so nothing is launched)

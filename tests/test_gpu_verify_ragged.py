@@ -96,3 +96,43 @@ def test_verify_b4_1m_with_ragged_counts_sampled():
     for b in (0, 3):
         k = q_lens[b]
         assert np.all(o[b][k:] == 0) and np.all(l[b][k:] == -np.inf)
+
+
+def test_dispatch_order_does_not_change_the_result():
+    """Requests dispatched longest first (or in any permutation) give the same bits as
+    request order: each workgroup's work does not depend on when it runs."""
+    w = Workload("order", batch=5, heads=32, q_tokens=2, context=None, context_range=(1, 1),
+                 page_size=64, permuted_pool=True, seed=71)
+    dw = materialize(w, seq_lens=np.array([200, 5000, 64, 3000, 1200], np.int32))
+
+    def run(order):
+        od = None if order is None else torch.tensor(order, dtype=torch.int32, device="cuda")
+        po, pl, _ = mla.decode_splitkv(dw.q8, dw.kv_pool8, dw.page_table, dw.seq_lens,
+                                       dw.q_scale, dw.kv_scale, w.softmax_scale,
+                                       dw.max_seq_len, 6, 0, order=od)
+        out, lse = mla.splitkv_combine(po, pl, 2, 32, dw.kv_scale)
+        torch.cuda.synchronize()
+        return _bf16(out), lse.cpu().numpy()
+    a = run(None)
+    for order in ([1, 3, 4, 0, 2], [4, 3, 2, 1, 0]):
+        b = run(order)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), order
+    _check(dw, *a, [2] * 5, range(5))
+
+
+def test_paged_b32_longest_first_sampled():
+    """The paged workload dispatched longest first, planned with the requests' total length
+    as the benchmark does: sampled requests against the oracle."""
+    dw = materialize(WORKLOADS["paged_b32"])
+    w = dw.w
+    S = mla.splitkv_plan(w.batch, w.q_tokens, w.heads, dw.max_seq_len,
+                         total_kv_tokens=dw.kv_tokens).num_splits
+    order = torch.from_numpy(np.argsort(-dw.seq_lens_host, kind="stable").astype(np.int32))
+    po, pl, _ = mla.decode_splitkv(dw.q8, dw.kv_pool8, dw.page_table, dw.seq_lens, dw.q_scale,
+                                   dw.kv_scale, w.softmax_scale, dw.max_seq_len, S, 0,
+                                   order=order.cuda())
+    out, lse = mla.splitkv_combine(po, pl, 1, w.heads, dw.kv_scale)
+    torch.cuda.synchronize()
+    lens = dw.seq_lens_host
+    picks = [int(np.argmin(lens)), int(np.argmax(lens)), 13]
+    _check(dw, _bf16(out), lse.cpu().numpy(), [1] * w.batch, picks)

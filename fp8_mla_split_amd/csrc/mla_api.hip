@@ -113,20 +113,22 @@ mla_status mla_quantize_fp8_sat_dynamic(const void* src_dev, int src_dtype, uint
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status mla_kv_append_fp8_sat(const float* new_kv_dev, uint8_t* kv_pool_dev, int64_t num_pages,
-                                 const int32_t* page_table_dev, const int32_t* seq_lens_dev,
-                                 int batch, int new_tokens, int page_size, int max_pages,
-                                 float kv_scale, void* stream) {
+mla_status mla_kv_append_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t* kv_pool_dev,
+                                 int64_t num_pages, const int32_t* page_table_dev,
+                                 const int32_t* seq_lens_dev, int batch, int new_tokens,
+                                 int page_size, int max_pages, float kv_scale, void* stream) {
   if (batch < 0 || new_tokens < 0 || page_size < 1 || max_pages < 1 || num_pages < 1 ||
-      !good_scale(kv_scale))
+      !good_scale(kv_scale) || (src_dtype != MLA_SRC_F32 && src_dtype != MLA_SRC_BF16))
     return MLA_ERR_INVALID_ARG;
   if (batch == 0 || new_tokens == 0) return MLA_OK;
   if (!new_kv_dev || !kv_pool_dev || !page_table_dev || !seq_lens_dev) return MLA_ERR_INVALID_ARG;
-  if (((uintptr_t)new_kv_dev & 3) != 0) return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)new_kv_dev & (src_dtype == MLA_SRC_BF16 ? 1 : 3)) != 0)
+    return MLA_ERR_INVALID_ARG;
   if ((int64_t)batch * new_tokens > 0x7FFFFFFFLL ||
       (int64_t)max_pages * page_size > 0x7FFFFFFFLL)
     return MLA_ERR_UNSUPPORTED;
-  const hipError_t e = mla::launch_kv_append(new_kv_dev, kv_pool_dev, num_pages, page_table_dev,
+  const hipError_t e = mla::launch_kv_append(new_kv_dev, src_dtype == MLA_SRC_BF16, kv_pool_dev,
+                                             num_pages, page_table_dev,
                                              seq_lens_dev, batch, new_tokens, page_size,
                                              max_pages, kv_scale, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

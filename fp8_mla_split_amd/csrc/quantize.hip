@@ -89,14 +89,19 @@ __global__ __launch_bounds__(kThreads) void quantize_scalar(const float* __restr
     dst[i] = encode1(__fdiv_rn(src[i], scale));
 }
 
+// bf16 sources hold the upper halves of fp32 patterns.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
 // ---- Appending a decode step's new KV rows to the paged FP8 cache ----------------------
 // New token t of request b (of T) is logical position n = seq_lens[b] - T + t and goes to row
 // n % P of page page_table[b, n / P].  One thread per 16 columns of a 576-wide row (36 per
-// row: four 16-B fp32 loads, one 16-B store), or per column where a buffer is not 16-byte
-// aligned.  Positions past the page table and page ids outside the pool are skipped, so a
-// bad device-side length or table entry cannot write outside the pool.
-template <bool Vec>
-__global__ __launch_bounds__(kThreads) void kv_append(const float* __restrict__ src,
+// row: 64 or 32 source bytes, one 16-B store), or per column where a buffer is not 16-byte
+// aligned.  Sources are fp32 or bf16 (the upper half of an fp32 pattern, widened exactly).
+// Positions past the page table and page ids outside the pool are skipped, so a bad
+// device-side length or table entry cannot write outside the pool.
+template <bool Vec, bool Bf16>
+__global__ __launch_bounds__(kThreads) void kv_append(const void* __restrict__ src,
                                                       uint8_t* __restrict__ pool,
                                                       const int32_t* __restrict__ page_table,
                                                       const int32_t* __restrict__ seq_lens,
@@ -114,22 +119,36 @@ __global__ __launch_bounds__(kThreads) void kv_append(const float* __restrict__ 
     const int64_t page = page_table[(int64_t)b * max_pages + n / page_size];
     if (page < 0 || page >= num_pages) continue;
     uint8_t* d = pool + (page * page_size + n % page_size) * kD + c * kPer;
-    const float* x = src + row * kD + c * kPer;
+    const int64_t e0 = row * kD + c * kPer;  // first source element
     if constexpr (Vec) {
-      const float4* x4 = (const float4*)x;
-      const float4 a = x4[0], bb = x4[1], cc = x4[2], dd = x4[3];
-      uint4 o;
-      o.x = encode4(__fdiv_rn(a.x, scale), __fdiv_rn(a.y, scale), __fdiv_rn(a.z, scale),
-                    __fdiv_rn(a.w, scale));
-      o.y = encode4(__fdiv_rn(bb.x, scale), __fdiv_rn(bb.y, scale), __fdiv_rn(bb.z, scale),
-                    __fdiv_rn(bb.w, scale));
-      o.z = encode4(__fdiv_rn(cc.x, scale), __fdiv_rn(cc.y, scale), __fdiv_rn(cc.z, scale),
-                    __fdiv_rn(cc.w, scale));
-      o.w = encode4(__fdiv_rn(dd.x, scale), __fdiv_rn(dd.y, scale), __fdiv_rn(dd.z, scale),
-                    __fdiv_rn(dd.w, scale));
-      *(uint4*)d = o;
+      float x[16];
+      if constexpr (Bf16) {
+        const uint4* w = (const uint4*)((const uint16_t*)src + e0);
+        const uint4 a = w[0], bb = w[1];
+        const uint32_t ws[8] = {a.x, a.y, a.z, a.w, bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          x[2 * k] = bf16_lo(ws[k]);
+          x[2 * k + 1] = bf16_hi(ws[k]);
+        }
+      } else {
+        const float4* x4 = (const float4*)((const float*)src + e0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 a = x4[k];
+          x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
+        }
+      }
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = encode4(__fdiv_rn(x[4 * k], scale), __fdiv_rn(x[4 * k + 1], scale),
+                       __fdiv_rn(x[4 * k + 2], scale), __fdiv_rn(x[4 * k + 3], scale));
+      *(uint4*)d = make_uint4(o[0], o[1], o[2], o[3]);
     } else {
-      *d = encode1(__fdiv_rn(*x, scale));
+      const float x = Bf16 ? __uint_as_float((uint32_t)((const uint16_t*)src)[e0] << 16)
+                           : ((const float*)src)[e0];
+      *d = encode1(__fdiv_rn(x, scale));
     }
   }
 }
@@ -143,9 +162,6 @@ __global__ __launch_bounds__(kThreads) void kv_append(const float* __restrict__ 
 // so the result is NaN whenever the tensor holds one, as max|x| is.
 constexpr int kAmaxBlocks = 1024;
 
-// bf16 sources hold the upper halves of fp32 patterns.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
@@ -302,19 +318,22 @@ hipError_t launch_quantize_dynamic(const void* src, bool bf16, uint8_t* dst, int
               : launch_dynamic_t<false>(src, dst, n, scale_out, (uint32_t*)workspace, s);
 }
 
-hipError_t launch_kv_append(const float* src, uint8_t* pool, int64_t num_pages,
+hipError_t launch_kv_append(const void* src, bool bf16, uint8_t* pool, int64_t num_pages,
                             const int32_t* page_table, const int32_t* seq_lens, int batch,
                             int t_new, int page_size, int max_pages, float scale, hipStream_t s) {
   const bool vec = (uintptr_t)src % 16 == 0 && (uintptr_t)pool % 16 == 0;
   const int64_t units = (int64_t)batch * t_new * (vec ? kD / 16 : kD);
   const int grid = grid_for(units, 8192);
   const int64_t stride = (int64_t)grid * kThreads;
-  if (vec)
-    kv_append<true><<<grid, kThreads, 0, s>>>(src, pool, page_table, seq_lens, t_new, page_size,
-                                              max_pages, num_pages, units, stride, scale);
-  else
-    kv_append<false><<<grid, kThreads, 0, s>>>(src, pool, page_table, seq_lens, t_new, page_size,
-                                               max_pages, num_pages, units, stride, scale);
+#define MLA_APPEND(V, B)                                                                 \
+  kv_append<V, B><<<grid, kThreads, 0, s>>>(src, pool, page_table, seq_lens, t_new,      \
+                                            page_size, max_pages, num_pages, units, stride, \
+                                            scale)
+  if (vec && bf16) MLA_APPEND(true, true);
+  else if (vec) MLA_APPEND(true, false);
+  else if (bf16) MLA_APPEND(false, true);
+  else MLA_APPEND(false, false);
+#undef MLA_APPEND
   return hipGetLastError();
 }
 

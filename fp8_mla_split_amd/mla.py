@@ -50,8 +50,8 @@ _lib.mla_splitkv_combine_dev_scale.argtypes = [_vp, _vp, _i32, _i32, _i32, _i32,
 _lib.mla_quantize_fp8_sat_dynamic.restype = _i32
 _lib.mla_quantize_fp8_sat_dynamic.argtypes = [_vp, _i32, _vp, _i64, _vp, _vp, _i64, _vp]
 _lib.mla_kv_append_fp8_sat.restype = _i32
-_lib.mla_kv_append_fp8_sat.argtypes = [_vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _f32,
-                                       _vp]
+_lib.mla_kv_append_fp8_sat.argtypes = [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _f32, _vp]
 _lib.mla_hbm_read_probe.restype = _i32
 _lib.mla_hbm_read_probe.argtypes = [_vp, _i64, _vp, _i32, _vp]
 
@@ -138,9 +138,10 @@ def quantize_fp8_sat_dynamic(x: torch.Tensor, out: Optional[torch.Tensor] = None
 
 def kv_append_fp8_sat(new_kv: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.Tensor,
                       seq_lens: torch.Tensor, kv_scale: float) -> None:
-    """Quantise new_kv [B, T, 576] (fp32) into the paged cache kv_pool8 [pages, P, 576] at
-    positions seq_lens[b] - T + t (seq_lens already counts the new tokens)."""
-    _dev_tensor(new_kv, torch.float32, "new_kv")
+    """Quantise new_kv [B, T, 576] (fp32 or bf16) into the paged cache kv_pool8 [pages, P, 576]
+    at positions seq_lens[b] - T + t (seq_lens already counts the new tokens)."""
+    if not new_kv.is_cuda or new_kv.dtype not in _SRC_DTYPE or not new_kv.is_contiguous():
+        raise ValueError("new_kv must be a contiguous fp32 or bf16 tensor on the GPU")
     _dev_tensor(kv_pool8, torch.uint8, "kv_pool8")
     _dev_tensor(page_table, torch.int32, "page_table")
     _dev_tensor(seq_lens, torch.int32, "seq_lens")
@@ -151,7 +152,8 @@ def kv_append_fp8_sat(new_kv: torch.Tensor, kv_pool8: torch.Tensor, page_table: 
     if page_table.dim() != 2 or page_table.shape[0] != B or seq_lens.numel() != B:
         raise ValueError("page_table must be [B, max_pages] and seq_lens [B]")
     _check(_lib.mla_kv_append_fp8_sat(
-        _ptr(new_kv), _ptr(kv_pool8), kv_pool8.shape[0], _ptr(page_table), _ptr(seq_lens), B, T,
+        _ptr(new_kv), _SRC_DTYPE[new_kv.dtype], _ptr(kv_pool8), kv_pool8.shape[0],
+        _ptr(page_table), _ptr(seq_lens), B, T,
         kv_pool8.shape[1], page_table.shape[1], float(kv_scale), _stream(new_kv.device)),
         "mla_kv_append_fp8_sat")
 

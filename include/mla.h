@@ -111,19 +111,22 @@ mla_status mla_quantize_fp8_sat_dynamic(const void* src_dev, int src_dtype, uint
  * Positions outside [0, max_pages * page_size) and page ids outside [0, num_pages) are not
  * written; no other byte of the pool changes.  If two new rows name the same cache row,
  * which one lands is unspecified.
- *   new_kv_dev     fp32 [B, T, 576], device, 4-byte aligned (16-byte alignment of it and of
- *                  the pool takes the vector path); may not alias the pool.
+ *   new_kv_dev     [B, T, 576], device: fp32 (src_dtype MLA_SRC_F32, 4-byte aligned) or
+ *                  bf16 bit patterns (MLA_SRC_BF16, 2-byte aligned; widened exactly to fp32
+ *                  before the division); 16-byte alignment of it and of the pool takes the
+ *                  vector path; may not alias the pool.
  *   kv_pool_dev    uint8 [num_pages, page_size, 576], device.
  *   page_table_dev int32 [B, max_pages];  seq_lens_dev int32 [B]  (device).
  *   kv_scale       the cache's dequantisation scale: finite, > 0.
- * Errors: INVALID_ARG (negative sizes, page_size/max_pages/num_pages < 1, bad scale, NULL or
- * misaligned pointers with B*T > 0); UNSUPPORTED (B*T or max_pages*page_size >= 2^31); HIP.
+ * Errors: INVALID_ARG (negative sizes, page_size/max_pages/num_pages < 1, bad scale, unknown
+ * src_dtype, NULL or misaligned pointers with B*T > 0); UNSUPPORTED (B*T or
+ * max_pages*page_size >= 2^31); HIP.
  * B == 0 or T == 0 enqueues nothing.
  */
-mla_status mla_kv_append_fp8_sat(const float* new_kv_dev, uint8_t* kv_pool_dev, int64_t num_pages,
-                                 const int32_t* page_table_dev, const int32_t* seq_lens_dev,
-                                 int batch, int new_tokens, int page_size, int max_pages,
-                                 float kv_scale, void* stream);
+mla_status mla_kv_append_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t* kv_pool_dev,
+                                 int64_t num_pages, const int32_t* page_table_dev,
+                                 const int32_t* seq_lens_dev, int batch, int new_tokens,
+                                 int page_size, int max_pages, float kv_scale, void* stream);
 
 /*
  * Split planner ([A/MLA] item (3): at batch 1 a fixed split count leaves most compute units

@@ -38,7 +38,7 @@ def lib():
     L.mla_decode_splitkv_ex.argtypes = [v, v, v, v, v, v, v, i, i, i, i, i, i, f, f, v, v, f, i,
                                         i, v, v, i64, v]
     L.mla_quantize_fp8_sat_dynamic.argtypes = [v, i, v, i64, v, v, i64, v]
-    L.mla_kv_append_fp8_sat.argtypes = [v, v, i64, v, v, i, i, i, i, f, v]
+    L.mla_kv_append_fp8_sat.argtypes = [v, i, v, i64, v, v, i, i, i, i, f, v]
     return L
 
 
@@ -151,23 +151,28 @@ def test_dynamic_quantize_rejects_bad_arguments(lib):
 
 
 def test_kv_append_rejects_bad_arguments(lib):
-    a = lib.mla_kv_append_fp8_sat
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, -1, 1, 64, 4, 1.0, None) == INVALID
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, -1, 64, 4, 1.0, None) == INVALID
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 0, 4, 1.0, None) == INVALID
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 0, 1.0, None) == INVALID
-    assert a(FAKE, FAKE, 0, FAKE, FAKE, 2, 1, 64, 4, 1.0, None) == INVALID
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 0.0, None) == INVALID
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, float("inf"), None) == INVALID
+    def a(src, pool, num_pages, pt, sl, B, T, P, maxp, scale, dtype=0):
+        return lib.mla_kv_append_fp8_sat(src, dtype, pool, num_pages, pt, sl, B, T, P, maxp,
+                                         scale, None)
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, -1, 1, 64, 4, 1.0) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, -1, 64, 4, 1.0) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 0, 4, 1.0) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 0, 1.0) == INVALID
+    assert a(FAKE, FAKE, 0, FAKE, FAKE, 2, 1, 64, 4, 1.0) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 0.0) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, float("inf")) == INVALID
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 1.0, dtype=2) == INVALID   # unknown dtype
     for k in range(4):
         ptrs = [FAKE] * 4
         ptrs[k] = None
-        assert a(ptrs[0], ptrs[1], 8, ptrs[2], ptrs[3], 2, 1, 64, 4, 1.0, None) == INVALID
-    assert a(ctypes.c_void_p(0x1002), FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 1.0, None) == INVALID
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, 1 << 16, 1 << 16, 64, 4, 1.0, None) == UNSUPPORTED
-    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 1 << 16, 1 << 16, 1.0, None) == UNSUPPORTED
-    assert a(None, None, 8, None, None, 0, 1, 64, 4, 1.0, None) == OK    # empty batch
-    assert a(None, None, 8, None, None, 2, 0, 64, 4, 1.0, None) == OK    # no new tokens
+        assert a(ptrs[0], ptrs[1], 8, ptrs[2], ptrs[3], 2, 1, 64, 4, 1.0) == INVALID
+    assert a(ctypes.c_void_p(0x1002), FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 1.0) == INVALID
+    assert a(ctypes.c_void_p(0x1001), FAKE, 8, FAKE, FAKE, 2, 1, 64, 4, 1.0,
+             dtype=1) == INVALID                                               # bf16 alignment
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 1 << 16, 1 << 16, 64, 4, 1.0) == UNSUPPORTED
+    assert a(FAKE, FAKE, 8, FAKE, FAKE, 2, 1, 1 << 16, 1 << 16, 1.0) == UNSUPPORTED
+    assert a(None, None, 8, None, None, 0, 1, 64, 4, 1.0) == OK    # empty batch
+    assert a(None, None, 8, None, None, 2, 0, 64, 4, 1.0) == OK    # no new tokens
 
 
 def test_dev_scale_variants_reject_bad_arguments(lib):

@@ -8,7 +8,7 @@ import torch
 
 import fp8_mla_split_amd as mla
 from fp8_mla_split_amd.workload import materialize
-from oracle import append_kv_fp8, dynamic_quantize, quantize_e4m3_sat
+from oracle import append_kv_fp8, bf16_bits_to_f32, dynamic_quantize, quantize_e4m3_sat
 from synthetic import WORKLOADS, Workload, q_f32
 from tests import oracle_side as ors
 from tests.test_gpu_decode import _bf16, _compare, _oracle
@@ -98,7 +98,8 @@ def _append_case(rng, lens, t_new, page_size, max_pages, bad_page_req=None):
 
 @pytest.mark.parametrize("t_new,page_size", [(1, 64), (3, 32), (8, 64), (5, 96)])
 @pytest.mark.parametrize("offset", [0, 1])
-def test_append_bit_exact(t_new, page_size, offset):
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_append_bit_exact(t_new, page_size, offset, src):
     rng = np.random.default_rng(100 * t_new + page_size + offset)
     max_pages = 6
     cap = max_pages * page_size
@@ -107,11 +108,18 @@ def test_append_bit_exact(t_new, page_size, offset):
     pool, table, seq, new = _append_case(rng, lens, t_new, page_size, max_pages,
                                          bad_page_req=4)
     s = np.float32(2.0 * 4.5 / 448)
-    ref = append_kv_fp8(pool, table, seq, new, s)
     g_pool = torch.from_numpy(pool).cuda()
-    buf = torch.zeros(new.size + offset, dtype=torch.float32)
-    buf[offset:] = torch.from_numpy(new.reshape(-1))
-    g_new = buf.cuda()[offset:].view(new.shape)
+    if src == "bf16":  # the rows as bf16 patterns (truncated), widened exactly by the oracle
+        bits = (new.view(np.uint32) >> 16).astype(np.uint16)
+        ref = append_kv_fp8(pool, table, seq, bf16_bits_to_f32(bits), s)
+        buf = torch.zeros(new.size + offset, dtype=torch.int16)
+        buf[offset:] = torch.from_numpy(bits.reshape(-1).view(np.int16))
+        g_new = buf.cuda().view(torch.bfloat16)[offset:].view(new.shape)
+    else:
+        ref = append_kv_fp8(pool, table, seq, new, s)
+        buf = torch.zeros(new.size + offset, dtype=torch.float32)
+        buf[offset:] = torch.from_numpy(new.reshape(-1))
+        g_new = buf.cuda()[offset:].view(new.shape)
     mla.kv_append_fp8_sat(g_new, g_pool, torch.from_numpy(table).cuda(),
                           torch.from_numpy(seq).cuda(), float(s))
     torch.cuda.synchronize()

@@ -278,3 +278,32 @@ def test_device_scale_step_replays_in_a_graph():
         assert torch.equal(lse, ref_l), rep
         assert np.float32(qs.item()) == np.float32(dw.q_scale)
     _compare(dw, _bf16(out), lse.cpu().numpy(), _oracle(dw, [0, 1]))
+
+
+def test_dynamic_quantize_past_one_grid_of_work():
+    """More elements than one pass of the capped grid covers (8192 workgroups x 256 threads
+    x 16 values, and 1024 workgroups for the maxima), with a ragged tail: every element is
+    reached by the grid-stride loops and the maximum is the whole tensor's."""
+    n = (1 << 25) + (1 << 20) + 37
+    x = np.random.default_rng(12).standard_normal(n).astype(np.float32)
+    x[n - 5] = 97.25                                            # the maximum sits in the tail
+    codes, s = _dyn_gpu(x)
+    assert s == np.float32(97.25) / np.float32(448)
+    ref = quantize_e4m3_sat(x, s, threads=8)
+    assert np.array_equal(codes, ref)
+
+
+def test_append_many_rows_per_launch():
+    """A bulk append (4 requests x 16384 new rows, 36 threads per row: more units than one
+    grid of 8192 x 256 threads covers at once) into a permuted pool, against the oracle."""
+    rng = np.random.default_rng(13)
+    B, T, P, maxp = 4, 16384, 64, 272
+    lens = np.array([16384, 17000, 17408, 16500], np.int32)
+    pool, table, seq, new = _append_case(rng, list(lens), T, P, maxp)
+    s = np.float32(0.013)
+    ref = append_kv_fp8(pool, table, seq, new, s)
+    g_pool = torch.from_numpy(pool).cuda()
+    mla.kv_append_fp8_sat(torch.from_numpy(new).cuda(), g_pool, torch.from_numpy(table).cuda(),
+                          torch.from_numpy(seq).cuda(), float(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(g_pool.cpu().numpy(), ref)

@@ -41,3 +41,33 @@ def test_combine_matches_oracle(B, S, Sq, H):
     fin = np.isfinite(l_ref.reshape(B, R))
     assert np.array_equal(fin, np.isfinite(lse))
     assert np.max(np.abs(lse[fin] - l_ref.reshape(B, R)[fin])) <= 1e-5
+
+
+@pytest.mark.parametrize("S,H", [(1024, 32), (4096, 32)])
+def test_combine_many_splits_both_outputs(S, H):
+    """Up to the largest split count the combine accepts, with empty splits among them: the
+    bf16 output and the merged partial (fp16 in units of v_scale) against the oracle's merge
+    of the same values."""
+    rng = np.random.default_rng(S + H)
+    B, R = 1, H
+    v_scale = np.float32(0.02)
+    po = (rng.standard_normal((B, S, R, 512)) * 60).astype(np.float16)
+    pl = (rng.standard_normal((B, S, R)) * 6).astype(np.float32)
+    pl[:, 5::7, :] = -np.inf
+    po[:, 5::7, :, :] = np.nan
+    po64 = np.where(np.isnan(po), 0, po).astype(np.float64)
+    o_ref, l_ref = combine_fp64(po64, pl.astype(np.float64))          # units of v_scale
+    gpo, gpl = torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda()
+    out, lse = mla.splitkv_combine(gpo, gpl, 1, H, float(v_scale))
+    mo = torch.empty((B, R, 512), dtype=torch.float16, device="cuda")
+    ml = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    mla.splitkv_combine_partial(gpo, gpl, 1, H, mo, ml)
+    torch.cuda.synchronize()
+    o = bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)).reshape(B, R, 512)
+    ref = o_ref.reshape(B, R, 512) * float(v_scale)
+    assert np.all(np.abs(o - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+    m = mo.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(m - o_ref.reshape(B, R, 512)) <= np.abs(o_ref.reshape(B, R, 512))
+                  * 2.0 ** -10 + 1e-4)
+    for got in (lse.cpu().numpy().reshape(B, R), ml.cpu().numpy()):
+        assert np.max(np.abs(got - l_ref.reshape(B, R))) <= 1e-4

@@ -615,6 +615,18 @@ def main():
                   "split_sweep": split_sweep(a.workload),
                   "cache_prep": prep_probes(),
                   "context_parallel_share": context_parallel_share()}
+        others = {}
+        for key, kw in (("paged_b32", {"longest_first": True}), ("verify_b4_1m", {})):
+            r = run_workload(key, 20, 3, 0, 0, a.eager, **kw)
+            others[key] = {k: (round(r[k], 3) if isinstance(r[k], float) else r[k]) for k in (
+                "us_per_step", "decode_us", "combine_us", "num_splits", "kv_tokens",
+                "decode_gbps", "decode_mfma_tflops_algorithmic", "decode_mfma_tflops_executed")}
+            others[key]["decode_frac_of_hbm_peak"] = round(r["decode_gbps"] / HBM_PEAK_GBPS, 4)
+            if kw:
+                others[key]["order"] = "longest first"
+            print(f"[bench] {key}: {r['us_per_step']:.1f} us/step (decode {r['decode_us']:.1f} "
+                  f"us)", file=sys.stderr, flush=True)
+        extras["other_workloads"] = others
         dyn = run_workload(a.workload, a.steps, a.warmup, a.splits, a.rows_per_group, a.eager,
                            dev_scales=True)
         extras["device_scale_step"] = {k: round(dyn[k], 3) for k in (

@@ -102,6 +102,21 @@ def _time_graph(g, reps):
     return e0.elapsed_time(e1) / reps
 
 
+WARM_MS, BLOCK_MS, BLOCKS = 100.0, 40.0, 5
+
+
+def _time_graph_steady(g):
+    """Milliseconds of one replay of g in steady state: replays for at least WARM_MS of GPU
+    time first (clocks and caches settle), then BLOCKS timed blocks of at least BLOCK_MS each;
+    the median of the blocks' per-replay averages, and the number of replays timed."""
+    one = _time_graph(g, 1)
+    n_warm = max(2, int(WARM_MS / max(one, 1e-3)) + 1)
+    one = _time_graph(g, n_warm)
+    n = max(2, int(BLOCK_MS / max(one, 1e-3)) + 1)
+    blocks = [_time_graph(g, n) for _ in range(BLOCKS)]
+    return float(np.median(blocks)), n * BLOCKS
+
+
 def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_bytes=512 << 20,
                  dev_scales=False, q_lens=None, longest_first=False):
     """One decode step = Q quantise + split-KV decode + combine, timed over `steps` steps.
@@ -196,22 +211,27 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
         dec_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
         comb_us = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
     else:
+        # a graph holds a whole number of rotations over the KV copies, so that replays
+        # back to back still find each copy `copies` steps after its last use
+        gsteps = -(-steps // copies) * copies
         stream = torch.cuda.Stream()
         graphs = {}
         for name, fn in (("step", step), ("quantize", lambda i: quantize()), ("decode", decode),
                          ("combine", lambda i: combine())):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                for i in range(steps):
+                for i in range(gsteps):
                     fn(i)
             graphs[name] = g
-        for g in graphs.values():  # one untimed replay each
-            g.replay()
         torch.cuda.synchronize()
-        step_us = _time_graph(graphs["step"], 3) * 1e3 / steps
-        q_us = _time_graph(graphs["quantize"], 3) * 1e3 / steps
-        dec_us = _time_graph(graphs["decode"], 3) * 1e3 / steps
-        comb_us = _time_graph(graphs["combine"], 3) * 1e3 / steps
+        timed = {}
+        for name, g in graphs.items():
+            ms, reps = _time_graph_steady(g)
+            timed[name] = ms * 1e3 / gsteps
+            if name == "step":
+                res["graph_steps"], res["timed_steps"] = gsteps, gsteps * reps
+        step_us, q_us = timed["step"], timed["quantize"]
+        dec_us, comb_us = timed["decode"], timed["combine"]
         del graphs
 
     q_bytes = B * Sq * H * 576
@@ -240,16 +260,16 @@ def run_workload(key, steps, warmup, splits, rows_per_group, eager=False, min_by
     return res
 
 
-def _time_fn_graph(fn, n, reps=3):
-    """Microseconds per call of fn, n calls captured in one HIP graph, reps replays."""
+def _time_fn_graph(fn, n):
+    """Microseconds per call of fn, n calls captured in one HIP graph, replayed in steady
+    state (see _time_graph_steady)."""
     import torch
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for _ in range(n):
             fn()
-    g.replay()
-    return _time_graph(g, reps) * 1e3 / n
+    return _time_graph_steady(g)[0] * 1e3 / n
 
 
 def hbm_probes():
@@ -534,13 +554,18 @@ def cpu_baseline(key, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 200:
             break
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info())
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max(int(i.get("num_threads", 1)) for i in info)
+        blas = ", ".join(f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                         for i in info)
     except Exception:
         cores = len(os.sched_getaffinity(0))
     us = el / n * 1e6 * w.batch  # the oracle handles requests one after another
     return {"value": round(us, 1), "unit": "us/step", "cores": cores, "kind": "oracle",
+            "blas": blas,
             "sample": f"{n} full decode steps of request 0 of {w.name} (Q quantize + fp64 "
                       f"attention over all {int(lens[0])} positions and {w.heads} heads), "
                       f"{el:.1f} s of host time"}

@@ -23,24 +23,36 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into libmla.so; returns the library path."""
-    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU ops are kept out of the generated code
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-inline-asm", "-Wno-unused-command-line-argument",
-        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-        *srcs, "-o", tmp,
-    ]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip (one object each, in parallel) and link libmla.so; returns the
+    library path."""
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    flags = [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # packed fp32 VALU ops are kept out of the generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-inline-asm", "-Wno-unused-command-line-argument",
+        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+    ]
+    objs = [os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o") for src in srcs]
+    jobs = min(len(srcs), max(1, min(16, len(os.sched_getaffinity(0)))))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([hipcc(), *flags, "-c", so[0], "-o", so[1]], verbose),
+                    zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -235,6 +235,7 @@ static void launch_batch(const uint16_t* po, const float* pl, int batch, int spl
 hipError_t launch_combine(const uint16_t* po, const float* pl, int batch, int splits, int rows,
                           float v_scale, const float* v_scale_dev, uint16_t* out, float* out_lse,
                           int64_t out_b_stride, bool partial_out, hipStream_t s) {
+  clear_last_error();
   // As many loads in flight per wave as there are splits to cover, up to 16; from 64 splits
   // on, 8 per wave and twice the waves (up to 16) spread the loads wider (measured on MI355X:
   // 6.2 instead of 6.5 us at 256 splits, 3.9 instead of 4.4 at 64).

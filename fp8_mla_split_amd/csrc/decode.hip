@@ -535,11 +535,14 @@ void decode_kernel(const DecodeParams p) {
   // (computed for every lane, then selected: a branch here would make the compiler spill
   // around it and wait for the Q DMA)
   // A row whose query token t is past its request's count sees nothing (lim = -1), like a
-  // query with no visible position: its lse is -inf.
+  // query with no visible position: its lse is -inf.  Positions after the shard (ctx_after)
+  // lift the causal limit past the shard's end, which is then the limit: rows of a tile past
+  // L arrive as zeros and would otherwise count as scores of 0.
   const int t_r = (int)fast_div((uint32_t)R, p.div_heads);
-  const int lim_r = kRagged ? (t_r < qlen ? L + after - qlen + t_r : -1) : L - qlen + t_r;
+  const int lim_r =
+      kRagged ? (t_r < qlen ? min(L + after - qlen + t_r, L - 1) : -1) : L - qlen + t_r;
   const int lim = row_ok ? lim_r : 0x7FFFFFFF;
-  int lim_min = L + after - qlen + (int)fast_div((uint32_t)wrow0, p.div_heads);
+  int lim_min = min(L + after - qlen + (int)fast_div((uint32_t)wrow0, p.div_heads), L - 1);
   if constexpr (kRagged) {  // the wave's smallest limit is -1 if it holds an absent row
     const int t_hi = (int)fast_div((uint32_t)min(wrow0 + 31, M - 1), p.div_heads);
     if (t_hi >= qlen) lim_min = -1;
@@ -943,6 +946,7 @@ void decode_kernel(const DecodeParams p) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t s) {
+  clear_last_error();
   if (rows_per_group != kRows) return hipErrorInvalidValue;
   const int64_t units = (int64_t)p.batch * p.num_splits;
   const int64_t blocks = ((units + 7) / 8) * 8 * p.groups;

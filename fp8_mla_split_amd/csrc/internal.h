@@ -70,6 +70,10 @@ __host__ __device__ inline float score_scale_log2(float q_scale, float kv_scale,
   return (float)((double)q_scale * kv_scale * sm_scale * 1.4426950408889634);
 }
 
+// Every launch helper below starts here: it drops the thread's last HIP error, so that the
+// error it returns after its launches is theirs and not one left by an earlier, unrelated call.
+inline void clear_last_error() { (void)hipGetLastError(); }
+
 hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scale, hipStream_t s);
 int64_t dynamic_quantize_workspace_bytes();
 hipError_t launch_quantize_dynamic(const void* src, bool bf16, uint8_t* dst, int64_t n,

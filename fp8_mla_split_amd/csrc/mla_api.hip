@@ -84,6 +84,7 @@ const char* mla_status_string(mla_status s) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
     case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: break;
   }
   return "MLA_ERR_UNKNOWN";
 }

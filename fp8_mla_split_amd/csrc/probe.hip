@@ -41,6 +41,7 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* 
 
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int grid,
                              hipStream_t s) {
+  clear_last_error();
   read_probe_kernel<<<grid, kProbeThreads, 0, s>>>((const u32x4*)src, bytes / kProbeChunk, out);
   return hipGetLastError();
 }

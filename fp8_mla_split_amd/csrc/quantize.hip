@@ -291,6 +291,7 @@ int grid_for(int64_t units, int64_t cap) {
 template <bool Bf16>
 hipError_t launch_dynamic_t(const void* src, uint8_t* dst, int64_t n, float* scale_out,
                             uint32_t* partial, hipStream_t s) {
+  clear_last_error();
   const int esz = Bf16 ? 2 : 4;
   const bool src16 = (uintptr_t)src % 16 == 0;
   const int64_t words = src16 ? n * esz / 16 : n;
@@ -325,6 +326,7 @@ hipError_t launch_quantize_dynamic(const void* src, bool bf16, uint8_t* dst, int
 hipError_t launch_kv_append(const void* src, bool bf16, uint8_t* pool, int64_t num_pages,
                             const int32_t* page_table, const int32_t* seq_lens, int batch,
                             int t_new, int page_size, int max_pages, float scale, hipStream_t s) {
+  clear_last_error();
   const bool vec = (uintptr_t)src % 16 == 0 && (uintptr_t)pool % 16 == 0;
   const int64_t units = (int64_t)batch * t_new * (vec ? kD / 16 : kD);
   const int grid = grid_for(units, 8192);
@@ -343,6 +345,7 @@ hipError_t launch_kv_append(const void* src, bool bf16, uint8_t* pool, int64_t n
 
 hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scale,
                            hipStream_t s) {
+  clear_last_error();
   const bool aligned = ((uintptr_t)src % 16 == 0) && ((uintptr_t)dst % 16 == 0);
   int64_t done = 0;
   if ((uintptr_t)src % 16 == 0 && (uintptr_t)dst % 4 == 0 && n >= 4 && n < kSmallN) {

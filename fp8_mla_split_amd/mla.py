@@ -14,8 +14,7 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# FP8_MLA_LIB selects another build of the same library (same ABI), e.g. an instrumented one
-lib_path = os.environ.get("FP8_MLA_LIB") or os.path.join(_HERE, "libmla.so")
+lib_path = os.path.join(_HERE, "libmla.so")
 if not os.path.exists(lib_path):
     raise ImportError(f"{lib_path} is not built; run `python -m fp8_mla_split_amd.build`")
 _lib = ctypes.CDLL(lib_path)

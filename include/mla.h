@@ -45,10 +45,16 @@ typedef enum {
                               or non-positive scale */
   MLA_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported shapes (see each call) */
   MLA_ERR_WORKSPACE = 3,   /* partial buffers too small for the requested split count */
-  MLA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  /* Not statuses: these two bounds make every int a value of the type, so a code from
+     anywhere (an older or newer library, a corrupted variable) can be passed to
+     mla_status_string without undefined behaviour in C++. */
+  MLA_STATUS_INT_MIN_ = -2147483647 - 1,
+  MLA_STATUS_INT_MAX_ = 2147483647
 } mla_status;
 
-/* Human-readable name of a status code (static storage, never NULL). */
+/* Human-readable name of a status code; "MLA_ERR_UNKNOWN" for any other int (static
+   storage, never NULL). */
 const char* mla_status_string(mla_status s);
 
 /*

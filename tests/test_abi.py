@@ -313,3 +313,55 @@ def test_read_probe_rejects_bad_arguments(lib):
     assert r(FAKE, 1000, FAKE, 1, None) == INVALID       # not a multiple of 32 KiB
     assert r(ctypes.c_void_p(0x1004), 32768, FAKE, 1, None) == INVALID  # not 16-byte aligned
     assert r(FAKE, 0, FAKE, 1, None) == OK                # nothing to read
+
+
+def header_prototypes():
+    """{name: [parameter declarations]} of every function the header declares, whitespace
+    normalised."""
+    text = re.sub(r"/\*.*?\*/", "", open(HDR).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\((.*?)\)\s*;", text,
+                         flags=re.M | re.S):
+        params = [" ".join(p.split()) for p in m.group(2).split(",")]
+        protos[m.group(1)] = [p.replace(" *", "*").replace("* ", "*") for p in params]
+    return protos
+
+
+# The boundary as built, for the calls the path is made of.  It departs from the first
+# proposal of the interface in these places, each for a stated reason:
+#   - partial_o is fp16 (uint16_t bit patterns) in units of the KV scale, not fp32: it halves
+#     the partials' traffic, and every value lies in [-448, 448];
+#   - rows_per_group (query rows per workgroup) replaces a head-group count: a workgroup
+#     holds rows of several query tokens when a request has fewer than 128 heads;
+#   - partial_rows / partial_rows_capacity (entries of the partial buffers) replace a byte
+#     count: the two buffers have different element sizes;
+#   - the decode takes max_seq_len (the planner's input when num_splits is 0), the planner
+#     takes total_kv_tokens (mixed lengths) and the combine v_scale (fp16 partials are in
+#     KV-scale units);
+#   - streams are void* (a hipStream_t), so the header needs no HIP include.
+BOUNDARY = {
+    "mla_quantize_fp8_sat": ["const float*src_dev", "uint8_t*dst_dev", "int64_t n",
+                             "float scale", "void*stream"],
+    "mla_splitkv_plan": ["int batch", "int q_tokens", "int heads", "int max_seq_len",
+                         "int64_t total_kv_tokens", "int cu_count", "int*num_splits",
+                         "int*rows_per_group", "int64_t*partial_rows"],
+    "mla_decode_splitkv": ["const uint8_t*q8_dev", "const uint8_t*kv_pool_dev",
+                           "const int32_t*page_table_dev", "const int32_t*seq_lens_dev",
+                           "int batch", "int q_tokens", "int heads", "int page_size",
+                           "int max_pages", "int max_seq_len", "float q_scale",
+                           "float kv_scale", "float softmax_scale", "int num_splits",
+                           "int rows_per_group", "uint16_t*partial_o_dev",
+                           "float*partial_lse_dev", "int64_t partial_rows_capacity",
+                           "void*stream"],
+    "mla_splitkv_combine": ["const uint16_t*partial_o_dev", "const float*partial_lse_dev",
+                            "int batch", "int num_splits", "int q_tokens", "int heads",
+                            "float v_scale", "uint16_t*out_bf16_dev", "float*out_lse_dev",
+                            "void*stream"],
+    "mla_status_string": ["mla_status s"],
+}
+
+
+def test_boundary_prototypes_are_the_documented_ones():
+    protos = header_prototypes()
+    for name, params in BOUNDARY.items():
+        assert protos.get(name) == params, (name, protos.get(name))

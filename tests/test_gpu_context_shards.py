@@ -167,3 +167,35 @@ def test_shards_with_several_query_tokens(q_lens):
         k = q_lens[b]
         assert np.all(o[b][k:] == 0) and np.all(l[b][k:] == -np.inf)
         ors.check_output(o[b][:k], ref_o[:k], l[b][:k], ref_l[:k])
+
+
+@pytest.mark.parametrize("Sq,H", [(1, 32), (8, 16)], ids=["sq1", "sq8"])
+def test_uneven_shards_with_positions_after(Sq, H):
+    """Shards whose lengths are not multiples of the 32-token tile (1000, 100 and 1300
+    positions), each decoded in a padded buffer whose rows past the shard hold NaN bytes.
+    Every shard but the last is told how many positions follow it (ctx_after), which lifts
+    the causal limit past the shard's own end: positions past the shard must still count as
+    absent (not as zero rows).  Two-level merge, compared with the oracle over the whole
+    requests."""
+    lens_g = [1000, 100, 1300]
+    G, B = len(lens_g), 2
+    w = Workload("cp_uneven", batch=B, heads=H, q_tokens=Sq, context=sum(lens_g), seed=71)
+    dw = materialize(w)
+    R = Sq * H
+    go = torch.full((B, G, R, 512), float("nan"), dtype=torch.float16, device="cuda")
+    gl = torch.full((B, G, R), float("nan"), dtype=torch.float32, device="cuda")
+    off = 0
+    for g, Ls in enumerate(lens_g):
+        P = -(-Ls // 32) * 32
+        shard = torch.full((B, P, 576), 0x7F, dtype=torch.uint8, device="cuda")
+        shard[:, :Ls] = dw.kv_pool8[:, off:off + Ls]
+        table = torch.arange(B, dtype=torch.int32, device="cuda")[:, None].contiguous()
+        lens = torch.full((B,), Ls, dtype=torch.int32, device="cuda")
+        after = torch.full((B,), sum(lens_g[g + 1:]), dtype=torch.int32, device="cuda")
+        po, pl, _ = mla.decode_splitkv(dw.q8, shard, table, lens, dw.q_scale, dw.kv_scale,
+                                       w.softmax_scale, Ls, 3, 0, ctx_after=after)
+        mla.splitkv_combine_partial(po, pl, Sq, H, go[:, g], gl[:, g], G * R)
+        off += Ls
+    out, lse = mla.splitkv_combine(go, gl, Sq, H, dw.kv_scale)
+    torch.cuda.synchronize()
+    _compare(dw, _bf16(out), lse.cpu().numpy(), _oracle(dw, range(B)))

@@ -185,5 +185,5 @@ def test_paged_b32_sampled(full, with_total):
 def test_verify_b4_1m_sampled(full):
     dw = full("verify_b4_1m")
     o, l, _ = _run(dw)
-    heads = [0, 77, 127]
+    heads = [0, 40, 77, 127]  # one head in each wave's 32 rows
     _compare(dw, o, l, _oracle(dw, [0, 3], heads=heads), heads=heads)

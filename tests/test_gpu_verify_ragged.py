@@ -92,7 +92,7 @@ def test_verify_b4_1m_with_ragged_counts_sampled():
     dw = materialize(WORKLOADS["verify_b4_1m"])
     q_lens = [8, 5, 2, 7]
     o, l = _run(dw, q_lens, 0)
-    _check(dw, o, l, q_lens, [1, 2], heads=[0, 77, 127])
+    _check(dw, o, l, q_lens, [1, 2], heads=[0, 40, 77, 127])  # one head per wave
     for b in (0, 3):
         k = q_lens[b]
         assert np.all(o[b][k:] == 0) and np.all(l[b][k:] == -np.inf)

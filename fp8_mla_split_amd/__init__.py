@@ -6,7 +6,8 @@ first use of any public name, and that fails loudly if the library has not been 
 (``python -m fp8_mla_split_amd.build``).  The build module itself imports without it.
 """
 _PUBLIC = (
-    "MLAError", "Plan", "QUANTIZE_DYNAMIC_WORKSPACE_BYTES", "decode", "decode_splitkv",
+    "MLAError", "Plan", "QUANTIZE_DYNAMIC_WORKSPACE_BYTES", "decode", "decode_noalloc",
+    "decode_splitkv",
     "hbm_read_probe", "kv_append_fp8_sat",
     "lib_path", "quantize_fp8_sat", "quantize_fp8_sat_dynamic", "splitkv_combine",
     "splitkv_combine_partial",

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla.h"
+
 namespace mla {
 
 constexpr int kD = 576;    // KV row: 512 latent + 64 rope columns
@@ -73,6 +75,17 @@ __host__ __device__ inline float score_scale_log2(float q_scale, float kv_scale,
 // Every launch helper below starts here: it drops the thread's last HIP error, so that the
 // error it returns after its launches is theirs and not one left by an earlier, unrelated call.
 inline void clear_last_error() { (void)hipGetLastError(); }
+
+// The decode call's argument checks other than those of the partial buffers (no HIP call);
+// MLA_OK with batch == 0 means there is nothing to do.
+mla_status decode_check_args(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                             const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                             const int32_t* q_lens_dev, const int32_t* ctx_after_dev,
+                             const int32_t* order_dev, int batch, int q_tokens, int heads,
+                             int page_size, int max_pages, int max_seq_len, float q_scale,
+                             float kv_scale, const float* q_scale_dev,
+                             const float* kv_scale_dev, float softmax_scale, int num_splits,
+                             int rows_per_group);
 
 hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scale, hipStream_t s);
 int64_t dynamic_quantize_workspace_bytes();

@@ -157,6 +157,42 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
 
 }  // extern "C"
 
+namespace mla {
+
+mla_status decode_check_args(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                             const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                             const int32_t* q_lens_dev, const int32_t* ctx_after_dev,
+                             const int32_t* order_dev, int batch, int q_tokens, int heads,
+                             int page_size, int max_pages, int max_seq_len, float q_scale,
+                             float kv_scale, const float* q_scale_dev,
+                             const float* kv_scale_dev, float softmax_scale, int num_splits,
+                             int rows_per_group) {
+  const bool dev = q_scale_dev != nullptr;
+  if (batch < 0 || q_tokens < 1 || heads < 1 || page_size < 1 || max_pages < 1 ||
+      num_splits < 0 || rows_per_group < 0)
+    return MLA_ERR_INVALID_ARG;
+  if ((!dev && (!good_scale(q_scale) || !good_scale(kv_scale))) || !good_scale(softmax_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (batch == 0) return MLA_OK;
+  if (!q8_dev || !kv_pool_dev || !page_table_dev || !seq_lens_dev) return MLA_ERR_INVALID_ARG;
+  if (dev && (kv_scale_dev == nullptr || ((uintptr_t)q_scale_dev & 3) != 0 ||
+              ((uintptr_t)kv_scale_dev & 3) != 0))
+    return MLA_ERR_INVALID_ARG;
+  if (((uintptr_t)q_lens_dev & 3) != 0 || ((uintptr_t)ctx_after_dev & 3) != 0 ||
+      ((uintptr_t)order_dev & 3) != 0)
+    return MLA_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)q_tokens * heads;
+  if (M > kMaxRows || page_size % kTile != 0 ||
+      (int64_t)max_pages * page_size + 2LL * q_tokens > 0x7FFFFFFFLL - 64)
+    return MLA_ERR_UNSUPPORTED;
+  if (rows_per_group != 0 && rows_per_group != 128) return MLA_ERR_UNSUPPORTED;
+  if ((num_splits == 0 || rows_per_group == 0) && max_seq_len < 1) return MLA_ERR_INVALID_ARG;
+  if (num_splits > 65535) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+}  // namespace mla
+
 namespace {
 
 // Every decode entry point: host scales (q_scale_dev == NULL) or device scales; one query
@@ -170,30 +206,16 @@ mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
                          const float* kv_scale_dev, float softmax_scale, int num_splits,
                          int rows_per_group, uint16_t* partial_o_dev, float* partial_lse_dev,
                          int64_t partial_rows_capacity, void* stream) {
-  const bool dev = q_scale_dev != nullptr;
-  if (batch < 0 || q_tokens < 1 || heads < 1 || page_size < 1 || max_pages < 1 ||
-      num_splits < 0 || rows_per_group < 0 || partial_rows_capacity < 0)
-    return MLA_ERR_INVALID_ARG;
-  if ((!dev && (!good_scale(q_scale) || !good_scale(kv_scale))) || !good_scale(softmax_scale))
-    return MLA_ERR_INVALID_ARG;
-  if (batch == 0) return MLA_OK;
-  if (!q8_dev || !kv_pool_dev || !page_table_dev || !seq_lens_dev || !partial_o_dev ||
-      !partial_lse_dev)
-    return MLA_ERR_INVALID_ARG;
-  if (dev && (kv_scale_dev == nullptr || ((uintptr_t)q_scale_dev & 3) != 0 ||
-              ((uintptr_t)kv_scale_dev & 3) != 0))
-    return MLA_ERR_INVALID_ARG;
-  if (((uintptr_t)q_lens_dev & 3) != 0 || ((uintptr_t)ctx_after_dev & 3) != 0 ||
-      ((uintptr_t)order_dev & 3) != 0)
-    return MLA_ERR_INVALID_ARG;
+  if (partial_rows_capacity < 0) return MLA_ERR_INVALID_ARG;
+  const mla_status chk = mla::decode_check_args(
+      q8_dev, kv_pool_dev, page_table_dev, seq_lens_dev, q_lens_dev, ctx_after_dev, order_dev,
+      batch, q_tokens, heads, page_size, max_pages, max_seq_len, q_scale, kv_scale, q_scale_dev,
+      kv_scale_dev, softmax_scale, num_splits, rows_per_group);
+  if (chk != MLA_OK || batch == 0) return chk;
+  if (!partial_o_dev || !partial_lse_dev) return MLA_ERR_INVALID_ARG;
   const int64_t M = (int64_t)q_tokens * heads;
-  if (M > mla::kMaxRows || page_size % mla::kTile != 0 ||
-      (int64_t)max_pages * page_size + 2LL * q_tokens > 0x7FFFFFFFLL - 64)
-    return MLA_ERR_UNSUPPORTED;
-  if (rows_per_group != 0 && rows_per_group != 128) return MLA_ERR_UNSUPPORTED;
   int S = num_splits, r = rows_per_group;
   if (S == 0 || r == 0) {
-    if (max_seq_len < 1) return MLA_ERR_INVALID_ARG;
     int cu = 0;
     const mla_status st = device_cu_count(&cu);
     if (st != MLA_OK) return st;
@@ -233,7 +255,7 @@ mla_status decode_common(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
   p.div_groups = mla::make_fastdiv((uint32_t)groups);
   p.div_heads = mla::make_fastdiv((uint32_t)heads);
   p.div_tpp = mla::make_fastdiv((uint32_t)(page_size / mla::kTile));
-  p.c2 = dev ? 0.f : mla::score_scale_log2(q_scale, kv_scale, softmax_scale);
+  p.c2 = q_scale_dev != nullptr ? 0.f : mla::score_scale_log2(q_scale, kv_scale, softmax_scale);
   p.kv_scale = kv_scale;
   p.q_scale_dev = q_scale_dev;
   p.kv_scale_dev = kv_scale_dev;

@@ -51,6 +51,9 @@ _lib.mla_quantize_fp8_sat_dynamic.argtypes = [_vp, _i32, _vp, _i64, _vp, _vp, _i
 _lib.mla_kv_append_fp8_sat.restype = _i32
 _lib.mla_kv_append_fp8_sat.argtypes = [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
                                        _f32, _vp]
+_lib.mla_decode_noalloc.restype = _i32
+_lib.mla_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                    _f32, _f32, _i32, _vp, _vp, _vp]
 _lib.mla_hbm_read_probe.restype = _i32
 _lib.mla_hbm_read_probe.argtypes = [_vp, _i64, _vp, _i32, _vp]
 
@@ -310,6 +313,40 @@ def splitkv_combine_partial(partial_o: torch.Tensor, partial_lse: torch.Tensor, 
                                             heads, _ptr(out_o), _ptr(out_lse), int(stride),
                                             _stream(partial_o.device)),
            "mla_splitkv_combine_partial")
+
+
+def decode_noalloc(q8: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.Tensor,
+                   seq_lens: torch.Tensor, q_scale: float, kv_scale: float, softmax_scale: float,
+                   max_seq_len: int, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                   out_lse: Optional[torch.Tensor] = None, want_lse: bool = True):
+    """Decode + combine through mla_decode_noalloc (the split partials stay in the library's
+    own device array; the C call allocates nothing).  Returns ``(out bf16 [B, Sq, H, 512],
+    lse fp32 [B, Sq, H] or None)``; outputs not given are allocated here with torch."""
+    _dev_tensor(q8, torch.uint8, "q8")
+    _dev_tensor(kv_pool8, torch.uint8, "kv_pool8")
+    _dev_tensor(page_table, torch.int32, "page_table")
+    _dev_tensor(seq_lens, torch.int32, "seq_lens")
+    B, Sq, H, d = q8.shape
+    if d != D_KV or kv_pool8.dim() != 3 or kv_pool8.shape[2] != D_KV:
+        raise ValueError("q8 and kv_pool8 rows must be 576 wide")
+    dev = q8.device
+    if out is None:
+        out = torch.empty((B, Sq, H, D_V), dtype=torch.bfloat16, device=dev)
+    if out_lse is None and want_lse:
+        out_lse = torch.empty((B, Sq, H), dtype=torch.float32, device=dev)
+    _dev_tensor(out, torch.bfloat16, "out")
+    if out.numel() != B * Sq * H * D_V:
+        raise ValueError("out must be [B, Sq, H, 512]")
+    if out_lse is not None:
+        _dev_tensor(out_lse, torch.float32, "out_lse")
+        if out_lse.numel() != B * Sq * H:
+            raise ValueError("out_lse must be [B, Sq, H]")
+    _check(_lib.mla_decode_noalloc(
+        _ptr(q8), _ptr(kv_pool8), _ptr(page_table), _ptr(seq_lens), B, Sq, H,
+        kv_pool8.shape[1], page_table.shape[1], int(max_seq_len), float(q_scale),
+        float(kv_scale), float(softmax_scale), int(num_splits), _ptr(out), _ptr(out_lse),
+        _stream(dev)), "mla_decode_noalloc")
+    return out, out_lse
 
 
 def hbm_read_probe(buf: torch.Tensor, out: torch.Tensor, grid: int) -> None:

@@ -323,6 +323,33 @@ mla_status mla_splitkv_combine_dev_scale(const uint16_t* partial_o_dev,
                                          float* out_lse_dev, void* stream);
 
 /*
+ * mla_decode_splitkv followed by mla_splitkv_combine, allocating nothing: for callers that
+ * cannot allocate device memory (work captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc).  The caller passes the inputs and outputs; the split
+ * partials go to a device array of MLA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from that GPU's first call until the process ends (its address is looked up
+ * on the first call on each device; that call may load the library's code there).
+ *   Inputs, scales and num_splits as for mla_decode_splitkv (rows_per_group is the planner's
+ *   128); outputs as for mla_splitkv_combine: out_bf16_dev [B, Sq, H, 512] bf16 bits, out_lse_dev
+ *   [B, Sq, H] fp32 or NULL.
+ *   The partials need B * S * Sq * H * 1028 bytes (fp16 row + lse).  num_splits > 0 that does
+ *   not fit returns MLA_ERR_WORKSPACE; num_splits == 0 takes the planner's split count,
+ *   reduced until it fits (MLA_ERR_WORKSPACE if one split does not: B * Sq * H > 40,800).
+ *   The result equals that of the two calls with the same split count, bit for bit.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must not be issued; calls on one stream are ordered.
+ * Errors: as mla_decode_splitkv and mla_splitkv_combine, plus INVALID_ARG for a NULL
+ * out_bf16_dev with B > 0, WORKSPACE as above, HIP if the array's address cannot be found.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (40 * 1024 * 1024)
+mla_status mla_decode_noalloc(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,
+                              const int32_t* page_table_dev, const int32_t* seq_lens_dev,
+                              int batch, int q_tokens, int heads, int page_size, int max_pages,
+                              int max_seq_len, float q_scale, float kv_scale, float softmax_scale,
+                              int num_splits, uint16_t* out_bf16_dev, float* out_lse_dev,
+                              void* stream);
+
+/*
  * Diagnostics, not part of the decode path: streams bytes of buf_dev from HBM (16-byte
  * non-temporal loads, eight in flight per lane) and writes one XOR-fold word per workgroup
  * to out_dev[0 .. grid-1].  Benchmarks time it to state the read rate the decode kernel's KV

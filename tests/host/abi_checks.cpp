@@ -80,6 +80,28 @@ int main() {
          MLA_ERR_HIP);
   EXPECT(mla_hbm_read_probe(F, 32768, (uint32_t*)F, 1, nullptr) == MLA_ERR_HIP);
 
+  // the decode without allocation: argument checks, partials that do not fit, and calls
+  // that pass (they end where the array's address is looked up: no device here)
+  const int64_t kRows = (MLA_NOALLOC_SCRATCH_BYTES - 256) / 1028;
+  EXPECT(mla_decode_noalloc(u8, u8, i32, i32, 1, 1, 16, 64, 4, 256, 1.f, 1.f, 0.07f, 4, nullptr,
+                            nullptr, nullptr) == MLA_ERR_INVALID_ARG);
+  EXPECT(mla_decode_noalloc(nullptr, u8, i32, i32, 1, 1, 16, 64, 4, 256, 1.f, 1.f, 0.07f, 4, u16,
+                            nullptr, nullptr) == MLA_ERR_INVALID_ARG);
+  EXPECT(mla_decode_noalloc(u8, u8, i32, i32, 1, 1, 16, 64, 4, 256, nan, 1.f, 0.07f, 4, u16,
+                            nullptr, nullptr) == MLA_ERR_INVALID_ARG);
+  EXPECT(mla_decode_noalloc(u8, u8, i32, i32, 1, 1, 16, 48, 4, 256, 1.f, 1.f, 0.07f, 4, u16,
+                            nullptr, nullptr) == MLA_ERR_UNSUPPORTED);
+  EXPECT(mla_decode_noalloc(nullptr, nullptr, nullptr, nullptr, 0, 1, 16, 64, 4, 256, 1.f, 1.f,
+                            0.07f, 4, nullptr, nullptr, nullptr) == MLA_OK);
+  EXPECT(mla_decode_noalloc(u8, u8, i32, i32, 1, 1, 128, 64, 4, 256, 1.f, 1.f, 0.07f,
+                            (int)(kRows / 128) + 1, u16, f32, nullptr) == MLA_ERR_WORKSPACE);
+  EXPECT(mla_decode_noalloc(u8, u8, i32, i32, 1, 1, 128, 64, 4, 256, 1.f, 1.f, 0.07f,
+                            (int)(kRows / 128), u16, f32, nullptr) == MLA_ERR_HIP);
+  EXPECT(mla_decode_noalloc(u8, u8, i32, i32, (int)(kRows / 128) + 1, 1, 128, 64, 4, 256, 1.f,
+                            1.f, 0.07f, 0, u16, f32, nullptr) == MLA_ERR_WORKSPACE);
+  EXPECT(mla_decode_noalloc(u8, u8, i32, i32, 16, 1, 128, 64, 4, 256, 1.f, 1.f, 0.07f, 0, u16,
+                            f32, nullptr) == MLA_ERR_HIP);
+
   // planner: every shape gets a split count within [1, max(1, tiles / 2)] (and at most 4096),
   // 128 rows per group and partial_rows = B * S * Sq * H
   const int batches[] = {1, 2, 3, 16, 32, 64, 1024};

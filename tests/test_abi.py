@@ -39,6 +39,7 @@ def lib():
                                         i, v, v, i64, v]
     L.mla_quantize_fp8_sat_dynamic.argtypes = [v, i, v, i64, v, v, i64, v]
     L.mla_kv_append_fp8_sat.argtypes = [v, i, v, i64, v, v, i, i, i, i, f, v]
+    L.mla_decode_noalloc.argtypes = [v, v, v, v, i, i, i, i, i, i, f, f, f, i, v, v, v]
     return L
 
 
@@ -365,3 +366,18 @@ def test_boundary_prototypes_are_the_documented_ones():
     protos = header_prototypes()
     for name, params in BOUNDARY.items():
         assert protos.get(name) == params, (name, protos.get(name))
+
+
+def test_decode_noalloc_rejects_bad_arguments(lib):
+    d = lib.mla_decode_noalloc
+    rows = (40 * 1024 * 1024 - 256) // 1028        # partial rows the library's array holds
+
+    def dec(B=1, H=16, S=4, out=FAKE, q=FAKE, qs=1.0, P=64):
+        return d(q, FAKE, FAKE, FAKE, B, 1, H, P, 4, 256, qs, 1.0, 0.07, S, out, None, None)
+    assert dec(out=None) == INVALID
+    assert dec(q=None) == INVALID
+    assert dec(qs=0.0) == INVALID
+    assert dec(P=48) == UNSUPPORTED
+    assert dec(B=0, q=None, out=None) == OK                   # nothing to do
+    assert dec(H=128, S=rows // 128 + 1) == WORKSPACE         # that many splits do not fit
+    assert dec(B=rows // 128 + 1, H=128, S=0) == WORKSPACE    # not even one split fits

@@ -1,7 +1,8 @@
 """The library's host side under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
 
 tests/host/abi_checks.cpp drives every entry point of the C ABI (argument checks, calls that
-pass them, a sweep of the split planner) against the library's host source and
+pass them, a sweep of the split planner) against the library's host sources (the API and the
+no-allocation entry point) and
 tests/host/launch_stubs.cpp, which stands in for the kernel launchers; the sanitizers
 instrument host code only (each -fsanitize flag is bound to the host pass), so nothing runs
 on a GPU.
@@ -29,6 +30,7 @@ def test_host_code_is_clean_under_asan_and_ubsan(tmp_path):
            "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(ROOT, "fp8_mla_split_amd", "csrc"),
            os.path.join(ROOT, "fp8_mla_split_amd", "csrc", "mla_api.hip"),
+           os.path.join(ROOT, "fp8_mla_split_amd", "csrc", "noalloc.hip"),
            os.path.join(HERE, "host", "launch_stubs.cpp"),
            os.path.join(HERE, "host", "abi_checks.cpp"), "-o", str(exe)]
     res = subprocess.run(cmd, capture_output=True, text=True)

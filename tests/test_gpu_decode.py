@@ -56,6 +56,9 @@ def _compare(dw, got_o, got_l, ref, heads=None):
         go = got_o[b] if heads is None else got_o[b][:, heads]
         gl = got_l[b] if heads is None else got_l[b][:, heads]
         stats.append(ors.check_output(go, o_ref, gl, l_ref))
+    # measured errors of the sampled requests (shown with pytest -s)
+    print(f"[parity] {dw.w.name}: requests {list(ref)} max abs "
+          f"{max(s[0] for s in stats):.3e}, normalised L1 {max(s[1] for s in stats):.3e}")
     return stats
 
 
@@ -187,3 +190,65 @@ def test_verify_b4_1m_sampled(full):
     o, l, _ = _run(dw)
     heads = [0, 40, 77, 127]  # one head in each wave's 32 rows
     _compare(dw, o, l, _oracle(dw, [0, 3], heads=heads), heads=heads)
+
+
+def _place(kv8_rows, lens, page_size, seed):
+    """A pool holding the given per-request code rows: contiguous (page_size 0) or pages of
+    page_size tokens in a random permutation; unused rows hold NaN bytes."""
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    if page_size == 0:
+        P = max(64, -(-max(lens) // 64) * 64)
+        table = np.arange(B, dtype=np.int32)[:, None]
+        n_pages = B
+    else:
+        P = page_size
+        npg = [-(-L // P) for L in lens]
+        order = rng.permutation(int(sum(npg)))
+        table = np.zeros((B, max(npg)), np.int32)
+        off = 0
+        for b, k in enumerate(npg):
+            table[b, :k] = order[off:off + k]
+            off += k
+        n_pages = int(sum(npg))
+    pool = torch.full((n_pages, P, 576), 0x7F, dtype=torch.uint8, device="cuda")
+    flat = pool.view(-1, 576)
+    for b, L in enumerate(lens):
+        n = torch.arange(L, device="cuda")
+        tb = torch.from_numpy(table[b].astype(np.int64)).cuda()
+        flat[tb[n // P] * P + n % P] = kv8_rows[b]
+    return pool, torch.from_numpy(table).cuda()
+
+
+def test_output_is_bit_identical_across_layouts_and_batches():
+    """The decode's arithmetic depends on a request's data and its chunk partition only, not
+    on where its rows sit in memory or on what else is in the batch: contiguous, 64-token
+    pages and 96-token pages (three tiles: the steps straddle pages) give the same bits, and
+    so does a request decoded alone, in a batch, or dispatched in another order."""
+    lens = [3000, 777, 5123]
+    w = Workload("bitid", batch=3, heads=64, q_tokens=2, context=None, context_range=(1, 1),
+                 page_size=0, seed=91)
+    dw = materialize(w, seq_lens=np.array(lens, np.int32))
+    rows = [dw.kv_pool8[b, :L] for b, L in enumerate(lens)]
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    S, ml = 3, max(lens)
+
+    def run(pool, table, q8, seq_lens, order=None):
+        po, pl, _ = mla.decode_splitkv(q8, pool, table, seq_lens, dw.q_scale, dw.kv_scale,
+                                       w.softmax_scale, ml, S, 0, order=order)
+        out, lse = mla.splitkv_combine(po, pl, w.q_tokens, w.heads, dw.kv_scale)
+        torch.cuda.synchronize()
+        return out.view(torch.int16).cpu(), lse.cpu()
+
+    ref = run(*_place(rows, lens, 0, 1), dw.q8, sl)
+    for P in (64, 96, 128):
+        got = run(*_place(rows, lens, P, P), dw.q8, sl)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), P
+    order = torch.tensor([2, 0, 1], dtype=torch.int32, device="cuda")
+    got = run(*_place(rows, lens, 64, 7), dw.q8, sl, order=order)
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+    for b in range(3):   # alone, as a batch of one
+        alone = run(*_place([rows[b]], [lens[b]], 64, 11 + b), dw.q8[b:b + 1].contiguous(),
+                    sl[b:b + 1].contiguous())
+        assert torch.equal(alone[0], ref[0][b:b + 1]) and torch.equal(alone[1], ref[1][b:b + 1])
+    _compare(dw, _bf16(ref[0].view(torch.bfloat16).cuda()), ref[1].numpy(), _oracle(dw, [0, 1, 2]))

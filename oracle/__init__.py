@@ -43,6 +43,12 @@ Pinning (what each function is checked against, in ``tests/test_oracle_*``):
                          quantised rows in order; bytes outside the new rows never
                          change; one T-row append equals T one-row appends.
 
+* ``rope_rotate_f32`` / ``append_kv_rope_fp8``  the fp64 rotation of the same fp32 inputs
+                         (within the bound of three fp32 roundings); angle 0 is the plain
+                         append and a quarter turn maps (x0, x1) to (-x1, x0) exactly; a
+                         standard RoPE table agrees with torch's complex multiplication;
+                         latent columns and positions past the table are untouched.
+
 No function here is "parity unpinned".
 """
 from .e4m3 import (  # noqa: F401
@@ -52,7 +58,13 @@ from .e4m3 import (  # noqa: F401
     per_tensor_scale,
     quantize_e4m3_sat,
 )
-from .cache import append_kv_fp8, bf16_bits_to_f32, dynamic_quantize  # noqa: F401
+from .cache import (  # noqa: F401
+    append_kv_fp8,
+    append_kv_rope_fp8,
+    bf16_bits_to_f32,
+    dynamic_quantize,
+    rope_rotate_f32,
+)
 from .attention import (  # noqa: F401
     attention_fp64,
     combine_fp64,

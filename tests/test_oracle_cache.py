@@ -122,3 +122,90 @@ def test_out_of_range_positions_and_pages_are_skipped():
     mask = np.ones(pool.shape[:2], bool)
     mask[pt[0, 0], 0] = False
     assert np.array_equal(out[mask], pool[mask])
+
+
+# ---- RoPE fused with the append ---------------------------------------------------------
+
+from oracle import append_kv_rope_fp8, rope_rotate_f32  # noqa: E402
+
+
+def _ulp32(x):
+    x = np.abs(np.asarray(x, dtype=np.float32))
+    return np.spacing(np.maximum(x, np.float32(np.finfo(np.float32).tiny)))
+
+
+def test_rope_rotation_is_the_complex_product_within_three_roundings():
+    """Against the rotation of the same fp32 inputs in fp64 (products exact there): each
+    rotated value is within half an ulp of each of its two products and of itself."""
+    rng = np.random.default_rng(21)
+    for _ in range(50):
+        row = (rng.standard_normal(576) * rng.choice([1e-3, 1.0, 50.0])).astype(np.float32)
+        ang = rng.uniform(-np.pi, np.pi, 32)
+        c, s = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+        got = rope_rotate_f32(row, c, s)
+        x0, x1 = row[512::2].astype(np.float64), row[513::2].astype(np.float64)
+        c64, s64 = c.astype(np.float64), s.astype(np.float64)
+        ex0, ex1 = x0 * c64 - x1 * s64, x0 * s64 + x1 * c64
+        b0 = 0.5 * (_ulp32(x0 * c64) + _ulp32(x1 * s64) + _ulp32(ex0)) * 1.0001
+        b1 = 0.5 * (_ulp32(x0 * s64) + _ulp32(x1 * c64) + _ulp32(ex1)) * 1.0001
+        assert np.all(np.abs(got[512::2] - ex0) <= b0)
+        assert np.all(np.abs(got[513::2] - ex1) <= b1)
+        assert np.array_equal(got[:512], row[:512])          # latent columns untouched
+
+
+def test_rope_special_angles():
+    rng = np.random.default_rng(22)
+    row = rng.standard_normal(576).astype(np.float32)
+    one, zero = np.ones(32, np.float32), np.zeros(32, np.float32)
+    assert np.array_equal(rope_rotate_f32(row, one, zero), row)          # angle 0
+    q = rope_rotate_f32(row, zero, one)                                 # a quarter turn
+    assert np.array_equal(q[512::2], -row[513::2]) and np.array_equal(q[513::2], row[512::2])
+    h = rope_rotate_f32(row, -one, zero)                                # half a turn
+    assert np.array_equal(h[512:], -row[512:])
+
+
+def test_rope_with_a_standard_table_matches_torch_complex_product():
+    """A standard RoPE table (theta_i = 10000^(-2i/64), angle n theta_i) applied as the
+    complex product of adjacent column pairs, as torch computes it in float64."""
+    pos = np.arange(300)
+    theta = 10000.0 ** (-np.arange(32) * 2.0 / 64.0)
+    ang = pos[:, None] * theta[None, :]
+    cos_t, sin_t = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    rng = np.random.default_rng(23)
+    rows = rng.standard_normal((300, 576)).astype(np.float32)
+    got = np.stack([rope_rotate_f32(rows[n], cos_t[n], sin_t[n]) for n in range(300)])
+    z = torch.view_as_complex(torch.from_numpy(rows[:, 512:].astype(np.float64)).reshape(300, 32, 2))
+    w = torch.complex(torch.from_numpy(cos_t.astype(np.float64)), torch.from_numpy(sin_t.astype(np.float64)))
+    ref = torch.view_as_real(z * w).reshape(300, 64).numpy()
+    assert np.max(np.abs(got[:, 512:] - ref)) <= 4 * np.finfo(np.float32).eps * np.abs(ref).max()
+
+
+def test_rope_append_writes_the_rotated_rows_and_nothing_past_the_table():
+    rng = np.random.default_rng(24)
+    lens = np.array([2, 13, 40], np.int32)
+    pool, page_table, _ = _pool_case(rng, lens=tuple(int(x) for x in lens))
+    T = 3
+    new = (rng.standard_normal((3, T, 576)) * 2).astype(np.float32)
+    n_pos = int(lens.max()) - 1                  # the last position of the longest request is past it
+    ang = rng.uniform(-np.pi, np.pi, (n_pos, 32))
+    cos_t, sin_t = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    scale = np.float32(0.01)
+    got = append_kv_rope_fp8(pool, page_table, lens, new, scale, cos_t, sin_t)
+    P = pool.shape[1]
+    touched = np.zeros(pool.shape[:2], bool)
+    for b in range(3):
+        for t in range(T):
+            n = int(lens[b]) - T + t
+            if n < 0:
+                continue
+            page, r = page_table[b, n // P], n % P
+            if n >= n_pos:
+                assert np.array_equal(got[page, r], pool[page, r])     # past the table
+                continue
+            touched[page, r] = True
+            want = quantize_e4m3_sat(rope_rotate_f32(new[b, t], cos_t[n], sin_t[n]), scale)
+            assert np.array_equal(got[page, r], want)
+            # the latent part is the plain append's
+            plain = append_kv_fp8(pool, page_table, lens, new, scale)
+            assert np.array_equal(got[page, r, :512], plain[page, r, :512])
+    assert np.array_equal(got[~touched], pool[~touched])

@@ -71,3 +71,37 @@ def test_planned_split_count_reduced_to_fit():
     _compare(dw, _bf16(got[0]), got[1].cpu().numpy(), _oracle(dw, [0, 199]))
     with pytest.raises(mla.MLAError):                              # a given count that does not fit
         _noalloc(dw, fit + 1)
+
+
+def test_captured_in_a_graph_and_replayed():
+    """The use it is made for: the Q quantisation and the no-allocation decode captured into a
+    HIP graph (nothing to allocate, no memset), replayed three times with other work and
+    synchronisations in between; every replay equals the eager result bit for bit."""
+    dw = _workload("noalloc_graph", 2, 128, 1, [20000, 7000], 64, 84)
+    w = dw.w
+    from synthetic import q_f32
+    q32 = torch.from_numpy(q_f32(w)).cuda()
+    q8 = torch.empty(q32.shape, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, 1, w.heads, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, 1, w.heads), dtype=torch.float32, device="cuda")
+
+    def step():
+        mla.quantize_fp8_sat(q32, dw.q_scale, out=q8)
+        mla.decode_noalloc(q8, dw.kv_pool8, dw.page_table, dw.seq_lens, dw.q_scale, dw.kv_scale,
+                           w.softmax_scale, dw.max_seq_len, 0, out=out, out_lse=lse)
+    step()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    assert torch.equal(q8, dw.q8)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for k in range(3):
+        out.zero_()
+        lse.zero_()
+        _noalloc(_workload(f"noalloc_between_{k}", 1, 16, 1, [500 + 100 * k], 0, 85 + k), 2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _same((out, lse), ref)

@@ -328,7 +328,7 @@ def prep_probes():
     res = {}
     rng = np.random.default_rng(0)
 
-    def append_case(batch, t_new, max_pages, page_size=64, reps=200):
+    def append_case(batch, t_new, max_pages, page_size=64, reps=200, rope=False):
         pages = batch * max_pages
         pool = torch.zeros((pages, page_size, 576), dtype=torch.uint8, device="cuda")
         table = torch.from_numpy(rng.permutation(pages).astype(np.int32).reshape(
@@ -336,12 +336,24 @@ def prep_probes():
         lens = torch.from_numpy(rng.integers(t_new, max_pages * page_size + 1, size=batch)
                                 .astype(np.int32)).cuda()
         new = torch.randn((batch, t_new, 576), device="cuda")
-        us = _time_fn_graph(lambda: mla.kv_append_fp8_sat(new, pool, table, lens, 0.01), reps)
+        if rope:  # a standard table: theta_i = 10000^(-2i/64), one row per position
+            pos = torch.arange(max_pages * page_size, device="cuda", dtype=torch.float64)
+            theta = 10000.0 ** (-torch.arange(32, device="cuda", dtype=torch.float64) / 32.0)
+            ang = pos[:, None] * theta[None, :]
+            cos_t, sin_t = torch.cos(ang).float(), torch.sin(ang).float()
+            fn = lambda: mla.kv_append_rope_fp8_sat(new, pool, table, lens, 0.01, cos_t, sin_t)
+        else:
+            fn = lambda: mla.kv_append_fp8_sat(new, pool, table, lens, 0.01)
+        us = _time_fn_graph(fn, reps)
         return us, batch * t_new * 576
     us, n = append_case(32, 1, 2048)
     res["kv_append_b32_t1_us"] = round(us, 2)
     us, n = append_case(4, 8, 16384)
     res["kv_append_b4_t8_us"] = round(us, 2)
+    us, n = append_case(32, 1, 2048, rope=True)
+    res["kv_append_rope_b32_t1_us"] = round(us, 2)
+    us, n = append_case(4, 8, 16384, rope=True)
+    res["kv_append_rope_b4_t8_us"] = round(us, 2)
     us, n = append_case(16, 8192, 129, reps=20)
     res["kv_append_bulk_b16_t8192"] = {"us": round(us, 1), "gbps": round(5 * n / (us * 1e3), 1),
                                        "frac_of_hbm_peak": round(5 * n / (us * 1e3)

@@ -8,7 +8,7 @@ first use of any public name, and that fails loudly if the library has not been 
 _PUBLIC = (
     "MLAError", "Plan", "QUANTIZE_DYNAMIC_WORKSPACE_BYTES", "decode", "decode_noalloc",
     "decode_splitkv",
-    "hbm_read_probe", "kv_append_fp8_sat",
+    "hbm_read_probe", "kv_append_fp8_sat", "kv_append_rope_fp8_sat",
     "lib_path", "quantize_fp8_sat", "quantize_fp8_sat_dynamic", "splitkv_combine",
     "splitkv_combine_partial",
     "splitkv_plan", "status_string",

@@ -91,9 +91,13 @@ hipError_t launch_quantize(const float* src, uint8_t* dst, int64_t n, float scal
 int64_t dynamic_quantize_workspace_bytes();
 hipError_t launch_quantize_dynamic(const void* src, bool bf16, uint8_t* dst, int64_t n,
                                    float* scale_out, void* workspace, hipStream_t s);
+// rope_cos / rope_sin: NULL (no rotation) or fp32 [rope_positions, 32] tables of the rope
+// pairs' angles per position.
 hipError_t launch_kv_append(const void* src, bool bf16, uint8_t* pool, int64_t num_pages,
                             const int32_t* page_table, const int32_t* seq_lens, int batch,
-                            int t_new, int page_size, int max_pages, float scale, hipStream_t s);
+                            int t_new, int page_size, int max_pages, float scale,
+                            const float* rope_cos, const float* rope_sin, int64_t rope_positions,
+                            hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int rows_per_group, hipStream_t s);
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* out, int grid,
                              hipStream_t s);

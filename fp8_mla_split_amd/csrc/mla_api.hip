@@ -114,10 +114,15 @@ mla_status mla_quantize_fp8_sat_dynamic(const void* src_dev, int src_dtype, uint
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status mla_kv_append_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t* kv_pool_dev,
-                                 int64_t num_pages, const int32_t* page_table_dev,
-                                 const int32_t* seq_lens_dev, int batch, int new_tokens,
-                                 int page_size, int max_pages, float kv_scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+mla_status append_common(const void* new_kv_dev, int src_dtype, uint8_t* kv_pool_dev,
+                         int64_t num_pages, const int32_t* page_table_dev,
+                         const int32_t* seq_lens_dev, int batch, int new_tokens, int page_size,
+                         int max_pages, float kv_scale, const float* rope_cos_dev,
+                         const float* rope_sin_dev, int64_t rope_positions, void* stream) {
   if (batch < 0 || new_tokens < 0 || page_size < 1 || max_pages < 1 || num_pages < 1 ||
       !good_scale(kv_scale) || (src_dtype != MLA_SRC_F32 && src_dtype != MLA_SRC_BF16))
     return MLA_ERR_INVALID_ARG;
@@ -131,8 +136,38 @@ mla_status mla_kv_append_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t*
   const hipError_t e = mla::launch_kv_append(new_kv_dev, src_dtype == MLA_SRC_BF16, kv_pool_dev,
                                              num_pages, page_table_dev,
                                              seq_lens_dev, batch, new_tokens, page_size,
-                                             max_pages, kv_scale, (hipStream_t)stream);
+                                             max_pages, kv_scale, rope_cos_dev, rope_sin_dev,
+                                             rope_positions, (hipStream_t)stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_kv_append_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t* kv_pool_dev,
+                                 int64_t num_pages, const int32_t* page_table_dev,
+                                 const int32_t* seq_lens_dev, int batch, int new_tokens,
+                                 int page_size, int max_pages, float kv_scale, void* stream) {
+  return append_common(new_kv_dev, src_dtype, kv_pool_dev, num_pages, page_table_dev,
+                       seq_lens_dev, batch, new_tokens, page_size, max_pages, kv_scale, nullptr,
+                       nullptr, 0, stream);
+}
+
+mla_status mla_kv_append_rope_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t* kv_pool_dev,
+                                      int64_t num_pages, const int32_t* page_table_dev,
+                                      const int32_t* seq_lens_dev, int batch, int new_tokens,
+                                      int page_size, int max_pages, float kv_scale,
+                                      const float* rope_cos_dev, const float* rope_sin_dev,
+                                      int64_t rope_positions, void* stream) {
+  if (rope_positions < 1 || rope_positions > (int64_t(1) << 40)) return MLA_ERR_INVALID_ARG;
+  if (batch > 0 && new_tokens > 0 &&
+      (!rope_cos_dev || !rope_sin_dev || ((uintptr_t)rope_cos_dev & 3) != 0 ||
+       ((uintptr_t)rope_sin_dev & 3) != 0))
+    return MLA_ERR_INVALID_ARG;
+  return append_common(new_kv_dev, src_dtype, kv_pool_dev, num_pages, page_table_dev,
+                       seq_lens_dev, batch, new_tokens, page_size, max_pages, kv_scale,
+                       rope_cos_dev, rope_sin_dev, rope_positions, stream);
 }
 
 mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,

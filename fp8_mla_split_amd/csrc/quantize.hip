@@ -104,14 +104,33 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // aligned.  Sources are fp32 or bf16 (the upper half of an fp32 pattern, widened exactly).
 // Positions past the page table and page ids outside the pool are skipped, so a bad
 // device-side length or table entry cannot write outside the pool.
-template <bool Vec, bool Bf16>
+// RoPE on the way in (the Muse Spark Open page's kernel-work item that fuses RoPE with the
+// KV-cache write): rope pair (512 + 2i, 513 + 2i) of a new row is the complex number
+// x0 + i x1, multiplied by cos + i sin of its position's angle i (cos_t / sin_t: fp32
+// [positions, 32]).  Each product and sum is rounded on its own (no fused multiply-add), so
+// the rotated value, whose rounding decides its E4M3 code, is the same on every compiler.
+__device__ __forceinline__ void rope_pair(float& x0, float& x1, float c, float s) {
+  const float r0 = __fsub_rn(__fmul_rn(x0, c), __fmul_rn(x1, s));
+  const float r1 = __fadd_rn(__fmul_rn(x0, s), __fmul_rn(x1, c));
+  x0 = r0;
+  x1 = r1;
+}
+
+struct RopeTables {
+  const float* cos_t;  // NULL: no rotation
+  const float* sin_t;
+  int64_t positions;
+};
+
+template <bool Vec, bool Bf16, bool kRope>
 __global__ __launch_bounds__(kThreads) void kv_append(const void* __restrict__ src,
                                                       uint8_t* __restrict__ pool,
                                                       const int32_t* __restrict__ page_table,
                                                       const int32_t* __restrict__ seq_lens,
                                                       int t_new, int page_size, int max_pages,
                                                       int64_t num_pages, int64_t units,
-                                                      int64_t stride, float scale) {
+                                                      int64_t stride, float scale,
+                                                      RopeTables rope) {
   constexpr int kPer = Vec ? 16 : 1;
   constexpr int kUnitsPerRow = kD / kPer;
   for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units; u += stride) {
@@ -120,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void kv_append(const void* __restrict__ s
     const int b = (int)(row / t_new), t = (int)(row - (int64_t)b * t_new);
     const int64_t n = (int64_t)seq_lens[b] - t_new + t;
     if (n < 0 || n >= (int64_t)max_pages * page_size) continue;
+    if (kRope && n >= rope.positions) continue;  // no angle for it: not written
     const int64_t page = page_table[(int64_t)b * max_pages + n / page_size];
     if (page < 0 || page >= num_pages) continue;
     uint8_t* d = pool + (page * page_size + n % page_size) * kD + c * kPer;
@@ -143,6 +163,19 @@ __global__ __launch_bounds__(kThreads) void kv_append(const void* __restrict__ s
           x[4 * k] = a.x; x[4 * k + 1] = a.y; x[4 * k + 2] = a.z; x[4 * k + 3] = a.w;
         }
       }
+      if constexpr (kRope) {
+        if (c >= kDv / 16) {  // columns 16c .. 16c + 15 are rope pairs 8 (c - 32) ..
+          const int64_t a0 = n * 32 + 8 * (c - kDv / 16);
+          const float4 c0 = *(const float4*)(rope.cos_t + a0),
+                       c1 = *(const float4*)(rope.cos_t + a0 + 4);
+          const float4 s0 = *(const float4*)(rope.sin_t + a0),
+                       s1 = *(const float4*)(rope.sin_t + a0 + 4);
+          const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+          for (int k = 0; k < 8; ++k) rope_pair(x[2 * k], x[2 * k + 1], cs[k], sn[k]);
+        }
+      }
       uint32_t o[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
@@ -150,8 +183,20 @@ __global__ __launch_bounds__(kThreads) void kv_append(const void* __restrict__ s
                        __fdiv_rn(x[4 * k + 2], scale), __fdiv_rn(x[4 * k + 3], scale));
       *(uint4*)d = make_uint4(o[0], o[1], o[2], o[3]);
     } else {
-      const float x = Bf16 ? __uint_as_float((uint32_t)((const uint16_t*)src)[e0] << 16)
-                           : ((const float*)src)[e0];
+      auto elem = [&](int64_t e) __attribute__((always_inline)) {
+        return Bf16 ? __uint_as_float((uint32_t)((const uint16_t*)src)[e] << 16)
+                    : ((const float*)src)[e];
+      };
+      float x = elem(e0);
+      if constexpr (kRope) {
+        if (c >= kDv) {  // rope column: rotate it with its pair partner
+          const int j = c - kDv, i = j >> 1;
+          const int64_t ep = row * kD + kDv + 2 * i;
+          float x0 = elem(ep), x1 = elem(ep + 1);
+          rope_pair(x0, x1, rope.cos_t[n * 32 + i], rope.sin_t[n * 32 + i]);
+          x = (j & 1) ? x1 : x0;
+        }
+      }
       *d = encode1(__fdiv_rn(x, scale));
     }
   }
@@ -325,20 +370,33 @@ hipError_t launch_quantize_dynamic(const void* src, bool bf16, uint8_t* dst, int
 
 hipError_t launch_kv_append(const void* src, bool bf16, uint8_t* pool, int64_t num_pages,
                             const int32_t* page_table, const int32_t* seq_lens, int batch,
-                            int t_new, int page_size, int max_pages, float scale, hipStream_t s) {
+                            int t_new, int page_size, int max_pages, float scale,
+                            const float* rope_cos, const float* rope_sin, int64_t rope_positions,
+                            hipStream_t s) {
   clear_last_error();
-  const bool vec = (uintptr_t)src % 16 == 0 && (uintptr_t)pool % 16 == 0;
+  const bool rope = rope_cos != nullptr;
+  // the vector path loads a rope unit's eight angles as two 16-byte words per table
+  const bool vec = (uintptr_t)src % 16 == 0 && (uintptr_t)pool % 16 == 0 &&
+                   (!rope || ((uintptr_t)rope_cos % 16 == 0 && (uintptr_t)rope_sin % 16 == 0));
   const int64_t units = (int64_t)batch * t_new * (vec ? kD / 16 : kD);
   const int grid = grid_for(units, 8192);
   const int64_t stride = (int64_t)grid * kThreads;
-#define MLA_APPEND(V, B)                                                                 \
-  kv_append<V, B><<<grid, kThreads, 0, s>>>(src, pool, page_table, seq_lens, t_new,      \
-                                            page_size, max_pages, num_pages, units, stride, \
-                                            scale)
-  if (vec && bf16) MLA_APPEND(true, true);
-  else if (vec) MLA_APPEND(true, false);
-  else if (bf16) MLA_APPEND(false, true);
-  else MLA_APPEND(false, false);
+  const RopeTables tables{rope_cos, rope_sin, rope_positions};
+#define MLA_APPEND(V, B, R)                                                                 \
+  kv_append<V, B, R><<<grid, kThreads, 0, s>>>(src, pool, page_table, seq_lens, t_new,      \
+                                               page_size, max_pages, num_pages, units, stride, \
+                                               scale, tables)
+  if (rope) {
+    if (vec && bf16) MLA_APPEND(true, true, true);
+    else if (vec) MLA_APPEND(true, false, true);
+    else if (bf16) MLA_APPEND(false, true, true);
+    else MLA_APPEND(false, false, true);
+  } else {
+    if (vec && bf16) MLA_APPEND(true, true, false);
+    else if (vec) MLA_APPEND(true, false, false);
+    else if (bf16) MLA_APPEND(false, true, false);
+    else MLA_APPEND(false, false, false);
+  }
 #undef MLA_APPEND
   return hipGetLastError();
 }

@@ -54,6 +54,9 @@ _lib.mla_kv_append_fp8_sat.argtypes = [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _i3
 _lib.mla_decode_noalloc.restype = _i32
 _lib.mla_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                     _f32, _f32, _i32, _vp, _vp, _vp]
+_lib.mla_kv_append_rope_fp8_sat.restype = _i32
+_lib.mla_kv_append_rope_fp8_sat.argtypes = [_vp, _i32, _vp, _i64, _vp, _vp, _i32, _i32, _i32,
+                                            _i32, _f32, _vp, _vp, _i64, _vp]
 _lib.mla_hbm_read_probe.restype = _i32
 _lib.mla_hbm_read_probe.argtypes = [_vp, _i64, _vp, _i32, _vp]
 
@@ -158,6 +161,33 @@ def kv_append_fp8_sat(new_kv: torch.Tensor, kv_pool8: torch.Tensor, page_table: 
         _ptr(page_table), _ptr(seq_lens), B, T,
         kv_pool8.shape[1], page_table.shape[1], float(kv_scale), _stream(new_kv.device)),
         "mla_kv_append_fp8_sat")
+
+
+def kv_append_rope_fp8_sat(new_kv: torch.Tensor, kv_pool8: torch.Tensor, page_table: torch.Tensor,
+                           seq_lens: torch.Tensor, kv_scale: float, rope_cos: torch.Tensor,
+                           rope_sin: torch.Tensor) -> None:
+    """kv_append_fp8_sat with each new row's rope pairs rotated first by the angle of its
+    position: rope_cos / rope_sin are fp32 [positions, 32] tables on the GPU."""
+    if not new_kv.is_cuda or new_kv.dtype not in _SRC_DTYPE or not new_kv.is_contiguous():
+        raise ValueError("new_kv must be a contiguous fp32 or bf16 tensor on the GPU")
+    _dev_tensor(kv_pool8, torch.uint8, "kv_pool8")
+    _dev_tensor(page_table, torch.int32, "page_table")
+    _dev_tensor(seq_lens, torch.int32, "seq_lens")
+    _dev_tensor(rope_cos, torch.float32, "rope_cos")
+    _dev_tensor(rope_sin, torch.float32, "rope_sin")
+    if new_kv.dim() != 3 or new_kv.shape[2] != D_KV or kv_pool8.dim() != 3 or \
+            kv_pool8.shape[2] != D_KV:
+        raise ValueError("new_kv and kv_pool8 rows must be 576 wide")
+    if rope_cos.dim() != 2 or rope_cos.shape[1] != 32 or rope_sin.shape != rope_cos.shape:
+        raise ValueError("rope_cos and rope_sin must both be [positions, 32]")
+    B, T = new_kv.shape[0], new_kv.shape[1]
+    if page_table.dim() != 2 or page_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("page_table must be [B, max_pages] and seq_lens [B]")
+    _check(_lib.mla_kv_append_rope_fp8_sat(
+        _ptr(new_kv), _SRC_DTYPE[new_kv.dtype], _ptr(kv_pool8), kv_pool8.shape[0],
+        _ptr(page_table), _ptr(seq_lens), B, T, kv_pool8.shape[1], page_table.shape[1],
+        float(kv_scale), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+        _stream(new_kv.device)), "mla_kv_append_rope_fp8_sat")
 
 
 def _dev_scale(t, name: str) -> bool:

@@ -9,6 +9,8 @@
  *            (3) 64-way split-KV, (4) native saturating FP8 conversion.
  *   [B]      the ai.newsbites.today page "LMSYS、NVIDIA Rubin向けの高速化成果を発表", section
  *            "MLAアテンションのパイプライン深化".
+ *   [C]      the theainews.cc page on Muse Spark Open, section "内核优化:解码吞吐 3 倍", item
+ *            "RoPE 与 KV 缓存写入融合" (RoPE applied in the kernel that writes the decode KV).
  *
  * Problem (the pages' statement, in our words): long-context MLA decode mostly waits on
  * reading the KV cache from HBM ([A/MLA] (1), [B]).  Q and KV are first converted to FP8
@@ -133,6 +135,32 @@ mla_status mla_kv_append_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t*
                                  int64_t num_pages, const int32_t* page_table_dev,
                                  const int32_t* seq_lens_dev, int batch, int new_tokens,
                                  int page_size, int max_pages, float kv_scale, void* stream);
+
+/*
+ * mla_kv_append_fp8_sat with the rotary position embedding applied on the way in ([C]: RoPE
+ * fused with the KV-cache write, so no separate kernel rotates the new rows first).  The new
+ * rows carry the rope part unrotated; for new token t of request b at position
+ * n = seq_lens_dev[b] - T + t, the 32 pairs of adjacent rope columns (512 + 2i, 513 + 2i) are
+ * rotated as complex numbers by the angle of pair i at position n:
+ *   r0 = fl(fl(x0 * c) - fl(x1 * s)),   r1 = fl(fl(x0 * s) + fl(x1 * c)),
+ *   c = rope_cos_dev[n * 32 + i],  s = rope_sin_dev[n * 32 + i]
+ * in fp32 with every product and sum rounded on its own (no fused multiply-add), then the whole
+ * 576-wide row is quantised and stored exactly as mla_kv_append_fp8_sat does (the 512 latent
+ * columns are not rotated).  A position n >= rope_positions is not written (as a position past
+ * the page table).
+ *   rope_cos_dev, rope_sin_dev : fp32 [rope_positions, 32], device, 4-byte aligned (16-byte
+ *                                aligned ones take the vector path): the caller's angle tables,
+ *                                so any frequency schedule can be used.
+ *   rope_positions            : rows of the tables, >= 1.
+ * Other arguments, conventions and errors as mla_kv_append_fp8_sat, plus INVALID_ARG for
+ * NULL or misaligned tables (with B*T > 0) and rope_positions < 1.
+ */
+mla_status mla_kv_append_rope_fp8_sat(const void* new_kv_dev, int src_dtype, uint8_t* kv_pool_dev,
+                                      int64_t num_pages, const int32_t* page_table_dev,
+                                      const int32_t* seq_lens_dev, int batch, int new_tokens,
+                                      int page_size, int max_pages, float kv_scale,
+                                      const float* rope_cos_dev, const float* rope_sin_dev,
+                                      int64_t rope_positions, void* stream);
 
 /*
  * Split planner ([A/MLA] item (3): at batch 1 a fixed split count leaves most compute units

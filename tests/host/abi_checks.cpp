@@ -43,6 +43,12 @@ int main() {
   EXPECT(mla_kv_append_fp8_sat(F, 0, u8, 8, i32, i32, 2, 1, 64, 4, 1.f, nullptr) == MLA_ERR_HIP);
   EXPECT(mla_kv_append_fp8_sat(F, 0, u8, 8, i32, i32, 1 << 16, 1 << 16, 64, 4, 1.f, nullptr) ==
          MLA_ERR_UNSUPPORTED);
+  EXPECT(mla_kv_append_rope_fp8_sat(F, 0, u8, 8, i32, i32, 2, 1, 64, 4, 1.f, f32, f32, 100,
+                                    nullptr) == MLA_ERR_HIP);
+  EXPECT(mla_kv_append_rope_fp8_sat(F, 1, u8, 8, i32, i32, 2, 1, 64, 4, 1.f, nullptr, f32, 100,
+                                    nullptr) == MLA_ERR_INVALID_ARG);
+  EXPECT(mla_kv_append_rope_fp8_sat(F, 0, u8, 8, i32, i32, 2, 1, 64, 4, 1.f, f32, f32, 0,
+                                    nullptr) == MLA_ERR_INVALID_ARG);
 
   // decode: bad arguments, unsupported shapes, workspace, then calls that reach the launch
   EXPECT(mla_decode_splitkv(u8, u8, i32, i32, 1, 1, 16, 64, 4, 256, 1.f, 1.f, 0.07f, 4, 128,

@@ -17,7 +17,8 @@ hipError_t launch_quantize_dynamic(const void*, bool, uint8_t*, int64_t, float*,
   return hipErrorNotSupported;
 }
 hipError_t launch_kv_append(const void*, bool, uint8_t*, int64_t, const int32_t*,
-                            const int32_t*, int, int, int, int, float, hipStream_t) {
+                            const int32_t*, int, int, int, int, float, const float*, const float*,
+                            int64_t, hipStream_t) {
   return hipErrorNotSupported;
 }
 hipError_t launch_decode(const DecodeParams& p, int, hipStream_t) {

@@ -40,6 +40,7 @@ def lib():
     L.mla_quantize_fp8_sat_dynamic.argtypes = [v, i, v, i64, v, v, i64, v]
     L.mla_kv_append_fp8_sat.argtypes = [v, i, v, i64, v, v, i, i, i, i, f, v]
     L.mla_decode_noalloc.argtypes = [v, v, v, v, i, i, i, i, i, i, f, f, f, i, v, v, v]
+    L.mla_kv_append_rope_fp8_sat.argtypes = [v, i, v, i64, v, v, i, i, i, i, f, v, v, i64, v]
     return L
 
 
@@ -381,3 +382,16 @@ def test_decode_noalloc_rejects_bad_arguments(lib):
     assert dec(B=0, q=None, out=None) == OK                   # nothing to do
     assert dec(H=128, S=rows // 128 + 1) == WORKSPACE         # that many splits do not fit
     assert dec(B=rows // 128 + 1, H=128, S=0) == WORKSPACE    # not even one split fits
+
+
+def test_kv_append_rope_rejects_bad_arguments(lib):
+    def a(cos=FAKE, sin=FAKE, npos=100, B=2, T=1, src=FAKE, scale=1.0):
+        return lib.mla_kv_append_rope_fp8_sat(src, 0, FAKE, 8, FAKE, FAKE, B, T, 64, 4, scale,
+                                              cos, sin, npos, None)
+    assert a(cos=None) == INVALID
+    assert a(sin=None) == INVALID
+    assert a(cos=ctypes.c_void_p(0x1002)) == INVALID          # tables 4-byte aligned
+    assert a(npos=0) == INVALID
+    assert a(scale=0.0) == INVALID                            # the append's own checks
+    assert a(src=None) == INVALID
+    assert a(B=0, cos=None, sin=None) == OK                   # nothing to write

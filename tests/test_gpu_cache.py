@@ -8,7 +8,8 @@ import torch
 
 import fp8_mla_split_amd as mla
 from fp8_mla_split_amd.workload import materialize
-from oracle import append_kv_fp8, bf16_bits_to_f32, dynamic_quantize, quantize_e4m3_sat
+from oracle import (append_kv_fp8, append_kv_rope_fp8, bf16_bits_to_f32, dynamic_quantize,
+                    quantize_e4m3_sat)
 from synthetic import WORKLOADS, Workload, q_f32
 from tests import oracle_side as ors
 from tests.test_gpu_decode import _bf16, _compare, _oracle
@@ -125,6 +126,63 @@ def test_append_bit_exact(t_new, page_size, offset, src):
     torch.cuda.synchronize()
     got = g_pool.cpu().numpy()
     assert np.array_equal(got, ref)
+
+
+def _rope_tables(rng, positions, kind):
+    if kind == "standard":  # theta_i = 10000^(-2i/64), angle n theta_i
+        theta = 10000.0 ** (-np.arange(32) * 2.0 / 64.0)
+        ang = np.arange(positions)[:, None] * theta[None, :]
+    else:
+        ang = rng.uniform(-np.pi, np.pi, (positions, 32))
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@pytest.mark.parametrize("t_new,page_size", [(1, 64), (8, 64), (5, 96)])
+@pytest.mark.parametrize("offset", [0, 1])
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("tables", ["standard", "random", "random_unaligned"])
+def test_append_rope_bit_exact(t_new, page_size, offset, src, tables):
+    """RoPE fused with the append against the oracle: the rotated rope pairs and the plain
+    latent columns, quantised, at every new row's position; rows whose position is past the
+    angle tables, past the page table or on a page -1 are not written.  The vector path
+    (16-byte aligned rows and tables) and the per-column path (offset rows or tables)."""
+    rng = np.random.default_rng(7 * t_new + page_size + offset + len(tables))
+    max_pages = 6
+    cap = max_pages * page_size
+    lens = [100, max(t_new - 2, 0), cap, cap + 2, 50, 300]
+    pool, table, seq, new = _append_case(rng, lens, t_new, page_size, max_pages,
+                                         bad_page_req=4)
+    positions = 299                  # request 5's last position (299) is past the tables
+    cos_t, sin_t = _rope_tables(rng, positions, "standard" if tables == "standard" else "random")
+    s = np.float32(2.0 * 4.5 / 448)
+    g_pool = torch.from_numpy(pool).cuda()
+    if src == "bf16":
+        bits = (new.view(np.uint32) >> 16).astype(np.uint16)
+        ref = append_kv_rope_fp8(pool, table, seq, bf16_bits_to_f32(bits), s, cos_t, sin_t)
+        buf = torch.zeros(new.size + offset, dtype=torch.int16)
+        buf[offset:] = torch.from_numpy(bits.reshape(-1).view(np.int16))
+        g_new = buf.cuda().view(torch.bfloat16)[offset:].view(new.shape)
+    else:
+        ref = append_kv_rope_fp8(pool, table, seq, new, s, cos_t, sin_t)
+        buf = torch.zeros(new.size + offset, dtype=torch.float32)
+        buf[offset:] = torch.from_numpy(new.reshape(-1))
+        g_new = buf.cuda()[offset:].view(new.shape)
+    if tables == "random_unaligned":   # tables at a 4-byte (not 16-byte) aligned address
+        cbuf = torch.zeros(cos_t.size + 1, dtype=torch.float32, device="cuda")
+        sbuf = torch.zeros(sin_t.size + 1, dtype=torch.float32, device="cuda")
+        cbuf[1:] = torch.from_numpy(cos_t.reshape(-1)).cuda()
+        sbuf[1:] = torch.from_numpy(sin_t.reshape(-1)).cuda()
+        g_cos, g_sin = cbuf[1:].view(positions, 32), sbuf[1:].view(positions, 32)
+    else:
+        g_cos, g_sin = torch.from_numpy(cos_t).cuda(), torch.from_numpy(sin_t).cuda()
+    mla.kv_append_rope_fp8_sat(g_new, g_pool, torch.from_numpy(table).cuda(),
+                               torch.from_numpy(seq).cuda(), float(s), g_cos, g_sin)
+    torch.cuda.synchronize()
+    got = g_pool.cpu().numpy()
+    assert np.array_equal(got, ref)
+    # and the rope columns really moved: the rotated rows differ from a plain append
+    plain = append_kv_fp8(pool, table, seq, new if src == "f32" else bf16_bits_to_f32(bits), s)
+    assert not np.array_equal(ref[..., 512:], plain[..., 512:])
 
 
 def test_append_then_decode_reads_the_new_rows():

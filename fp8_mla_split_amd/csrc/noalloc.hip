@@ -45,8 +45,7 @@ mla_status scratch_on_current_device(uint8_t** out) {
   return MLA_OK;
 }
 
-// Split count whose partials fit the array: the given one (0 if it does not fit), or, for
-// num_splits == 0, the planner's choice reduced until it fits (0 if one split does not).
+// wanted if the partials of that many splits fit the array, else 0.
 int64_t splits_that_fit(int64_t rows_per_split, int64_t wanted) {
   const int64_t most = (kScratchBytes - 256) / (rows_per_split * kRowBytes);
   return wanted <= most ? wanted : 0;

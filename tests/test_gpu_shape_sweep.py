@@ -1,0 +1,60 @@
+"""Seeded sweep of decode shapes against the fp64 oracle (runs on an MI355X).
+
+Forty configurations drawn once from a fixed seed: batch 1-4, heads from 1 to 200, 1-8 query
+tokens (causal among them), lengths from 0 to 3000 drawn per request (so one call mixes
+empty, sub-tile, ragged and multi-chunk requests; at least one request per call is not
+empty), contiguous or paged pools (page sizes of an odd and an even number of 32-token
+tiles, permuted or in order), and the planner's split count or a fixed one from 1 to 40.
+Every request and head is compared element by element with the oracle, to the same contract
+as the named workloads.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+from fp8_mla_split_amd.workload import materialize
+from synthetic import Workload
+from tests.test_gpu_decode import _compare, _oracle, _run
+
+pytestmark = pytest.mark.gpu
+
+HEADS = (1, 2, 8, 16, 24, 48, 64, 100, 128, 200)
+PAGES = (0, 0, 32, 64, 96, 128, 256)
+
+
+def _cases(n=40, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 5))
+        H = int(rng.choice(HEADS))
+        Sq = int(rng.integers(1, 9)) if rng.random() < 0.4 else 1
+        while Sq * H > 512:
+            Sq = max(1, Sq // 2)
+        lens = rng.integers(0, 3001, size=B)
+        lens[rng.random(B) < 0.15] = 0
+        lens[rng.random(B) < 0.15] = rng.integers(1, 40)
+        if lens.max() == 0:  # an all-empty batch is its own edge case (test_gpu_decode.py)
+            lens[0] = 1 + (97 * i) % 3000
+        P = int(rng.choice(PAGES))
+        perm = bool(P and rng.random() < 0.7)
+        S = 0 if rng.random() < 0.4 else int(rng.integers(1, 41))
+        out.append((f"c{i:02d}_b{B}_h{H}_sq{Sq}_p{P}_s{S}", B, H, Sq, [int(x) for x in lens], P,
+                    perm, S))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_shape_sweep_matches_oracle(case):
+    name, B, H, Sq, lens, P, perm, S = case
+    print(f"[sweep] {name} lens {lens} permuted {perm}", flush=True)
+    w = Workload(name, batch=B, heads=H, q_tokens=Sq, context=None, context_range=(1, 1),
+                 page_size=P, permuted_pool=perm, seed=zlib.crc32(name.encode()) % 1000)
+    dw = materialize(w, seq_lens=np.array(lens, np.int32))
+    o, l, _ = _run(dw, S, 0)
+    ref = _oracle(dw, range(B))
+    _compare(dw, o, l, ref)

@@ -6,7 +6,9 @@ empty, sub-tile, ragged and multi-chunk requests; at least one request per call 
 empty), contiguous or paged pools (page sizes of an odd and an even number of 32-token
 tiles, permuted or in order), and the planner's split count or a fixed one from 1 to 40.
 Every request and head is compared element by element with the oracle, to the same contract
-as the named workloads.
+as the named workloads.  A second sweep of 24 draws does the same through the per-request
+path: draft counts from 0 to Sq per request (slots past a count must be O = 0, lse = -inf),
+a random dispatch order in half of them and device-side scales in some.
 """
 import zlib
 
@@ -58,3 +60,57 @@ def test_shape_sweep_matches_oracle(case):
     o, l, _ = _run(dw, S, 0)
     ref = _oracle(dw, range(B))
     _compare(dw, o, l, ref)
+
+
+def _ragged_cases(n=24, seed=20261204):
+    """Per-request draft counts (0..Sq), sometimes a dispatch order and device-side scales."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 6))
+        H = int(rng.choice(HEADS))
+        Sq = int(rng.integers(2, 9))
+        while Sq * H > 512:
+            Sq = max(2, Sq // 2)
+        lens = rng.integers(1, 3001, size=B)
+        lens[rng.random(B) < 0.2] = rng.integers(1, 12)
+        q_lens = rng.integers(0, Sq + 1, size=B)
+        P = int(rng.choice(PAGES))
+        S = 0 if rng.random() < 0.4 else int(rng.integers(1, 33))
+        order = rng.permutation(B) if rng.random() < 0.5 else None
+        dev = bool(rng.random() < 0.3)
+        out.append((f"r{i:02d}_b{B}_h{H}_sq{Sq}_p{P}_s{S}", B, H, Sq, [int(x) for x in lens],
+                    [int(x) for x in q_lens], P, S,
+                    None if order is None else [int(x) for x in order], dev))
+    return out
+
+
+RAGGED = _ragged_cases()
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_ragged_sweep_matches_oracle(case):
+    import torch
+
+    import fp8_mla_split_amd as mla
+    from tests.test_gpu_decode import _bf16
+    from tests.test_gpu_verify_ragged import _check
+
+    name, B, H, Sq, lens, q_lens, P, S, order, dev = case
+    print(f"[sweep] {name} lens {lens} q_lens {q_lens} order {order} device scales {dev}",
+          flush=True)
+    w = Workload(name, batch=B, heads=H, q_tokens=Sq, context=None, context_range=(1, 1),
+                 page_size=P, permuted_pool=bool(P), seed=zlib.crc32(name.encode()) % 1000)
+    dw = materialize(w, seq_lens=np.array(lens, np.int32))
+    if dev:
+        qs = torch.tensor([dw.q_scale], dtype=torch.float32, device="cuda")
+        ks = torch.tensor([dw.kv_scale], dtype=torch.float32, device="cuda")
+    else:
+        qs, ks = dw.q_scale, dw.kv_scale
+    ql = torch.tensor(q_lens, dtype=torch.int32, device="cuda")
+    od = None if order is None else torch.tensor(order, dtype=torch.int32, device="cuda")
+    po, pl, _ = mla.decode_splitkv(dw.q8, dw.kv_pool8, dw.page_table, dw.seq_lens, qs, ks,
+                                   w.softmax_scale, dw.max_seq_len, S, 0, q_lens=ql, order=od)
+    out, lse = mla.splitkv_combine(po, pl, Sq, H, ks)
+    torch.cuda.synchronize()
+    _check(dw, _bf16(out), lse.cpu().numpy(), q_lens, range(B))

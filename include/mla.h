@@ -22,8 +22,10 @@
  * Conventions for every entry point:
  *   - Pointers named *_dev are device pointers (HIP device memory); everything else is
  *     passed by value.  The caller allocates and frees every buffer; the library never
- *     allocates, frees or synchronises.  Its only state is a per-device cache of the
- *     compute-unit count, filled on first use.
+ *     allocates, frees or synchronises.  Its state is a per-device cache of the compute-unit
+ *     count, filled on first use, and, for mla_decode_noalloc only, one device array per GPU
+ *     (part of the library's code object, not allocated at run time) whose address it looks
+ *     up on that GPU's first such call.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  Work is
  *     enqueued asynchronously; device-side faults surface at the caller's next sync.
  *   - Every argument check runs before any HIP call, so invalid arguments are reported
@@ -198,9 +200,9 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
  *   partial_o[b,s,r,0:512] = sum_n softmax(z)_n * dec(KV8[n,0:512])
  * i.e. the chunk's attention output in units of kv_scale, so every value lies in [-448, 448]
  * and is stored as IEEE fp16 (round to nearest even); mla_splitkv_combine multiplies by
- * kv_scale again.  Chunk s holds tiles [s*c, (s+1)*c) of 32 tokens,
- * c = ceil(ceil(L_b/32) / S).  Where the lse is -inf (empty chunk, or no visible position)
- * the partial_o entry is unspecified.
+ * kv_scale again.  Chunk s holds tiles [s*c, (s+1)*c) of 32 tokens, c = 2 * ceil(ceil(L_b/64)
+ * / S), i.e. whole 64-token steps (the last chunks of a short request may be empty).  Where
+ * the lse is -inf (empty chunk, or no visible position) the partial_o entry is unspecified.
  *
  * Layouts (all contiguous, row-major):
  *   q8_dev          uint8 [B, Sq, H, 576]          e4m3 codes of Q

@@ -218,7 +218,9 @@ mla_status mla_splitkv_plan(int batch, int q_tokens, int heads, int max_seq_len,
  *   num_splits    : S >= 1, or 0 to take the planner's choice for (B, Sq, H, max_seq_len).
  *   rows_per_group: 128, or 0 to take the planner's choice.
  *   partial_rows_capacity : entries the partial buffers hold (see mla_splitkv_plan).
- * Supported: 1 <= Sq, Sq*H <= 65536, page_size a positive multiple of 32, max_pages >= 1.
+ * Supported: 1 <= Sq, Sq*H <= 65536, page_size a positive multiple of 32, max_pages >= 1,
+ * max_pages * page_size + 2 * Sq < 2^31 - 64, num_splits <= 65535 (mla_splitkv_combine
+ * merges at most 4096 in one call; the planner never picks more).
  * Errors: INVALID_ARG (NULL pointers with B > 0, negative sizes, scales not finite and > 0);
  * UNSUPPORTED (shape outside the supported set); WORKSPACE (B*S*Sq*H > capacity); HIP.
  * B == 0 enqueues nothing.

@@ -13,9 +13,10 @@
 // elements per iteration (four 16-B loads, one 16-B store); the grid strides over the array.
 // Tensors under 2^21 elements (one step's Q) take four elements per thread instead.
 //
-// The same encode serves two more entry points below: the append of a decode step's new KV
-// rows straight into their paged cache slots (fp32 or bf16 rows), and the quantisation whose
-// per-tensor scale (amax / 448) is taken from the data on the device in two passes.
+// The same encode serves the other entry points below: the append of a decode step's new KV
+// rows straight into their paged cache slots (fp32 or bf16 rows, optionally with RoPE applied
+// to their rope columns first), and the quantisation whose per-tensor scale (amax / 448) is
+// taken from the data on the device in two passes.
 #include "internal.h"
 
 namespace mla {

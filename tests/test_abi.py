@@ -395,3 +395,26 @@ def test_kv_append_rope_rejects_bad_arguments(lib):
     assert a(scale=0.0) == INVALID                            # the append's own checks
     assert a(src=None) == INVALID
     assert a(B=0, cos=None, sin=None) == OK                   # nothing to write
+
+
+def test_readme_c_example_compiles_against_the_header(tmp_path):
+    """The README's example of one decode step is valid C against include/mla.h."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    text = open(os.path.join(ROOT, "README.md")).read()
+    body = re.search(r"```c\n(.*?)```", text, flags=re.S).group(1)
+    src = tmp_path / "example.c"
+    src.write_text(
+        '#include "mla.h"\n'
+        "void example(int B, int Sq, int H, int max_len, const float* q_f32, uint8_t* q8,\n"
+        "             float q_scale, void* stream, const void* new_kv, uint8_t* pool,\n"
+        "             int64_t n_pages, const int32_t* table, const int32_t* lens, int max_pages,\n"
+        "             float kv_scale, float softmax_scale, uint16_t* partial_o,\n"
+        "             float* partial_lse, uint16_t* out_bf16, float* out_lse) {\n"
+        + body + "}\n")
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-I",
+                        os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

@@ -31,10 +31,17 @@ uint8_t* g_scratch[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
 std::once_flag g_scratch_once[kMaxDevices];
 
-// The array's device address on the current device, looked up on the first call there.
-mla_status scratch_on_current_device(uint8_t** out) {
+// The array's device address on the current device, looked up on the first call there.  The
+// kernels run on the stream's device, so a stream of another device is refused (its kernels
+// would be handed this device's address).
+mla_status scratch_on_current_device(hipStream_t stream, uint8_t** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MLA_ERR_HIP;
+    if (sdev != dev) return MLA_ERR_INVALID_ARG;
+  }
   std::call_once(g_scratch_once[dev], [dev] {
     void* ptr = nullptr;
     g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
@@ -82,7 +89,7 @@ extern "C" mla_status mla_decode_noalloc(const uint8_t* q8_dev, const uint8_t* k
     while (S > 1 && splits_that_fit(rows_per_split, S) == 0) --S;
   }
   uint8_t* base = nullptr;
-  const mla_status sst = scratch_on_current_device(&base);
+  const mla_status sst = scratch_on_current_device((hipStream_t)stream, &base);
   if (sst != MLA_OK) return sst;
   // partial outputs first, their lse after them (256-byte aligned)
   const int64_t entries = rows_per_split * S;

@@ -370,8 +370,10 @@ mla_status mla_splitkv_combine_dev_scale(const uint16_t* partial_o_dev,
  *   The result equals that of the two calls with the same split count, bit for bit.
  * Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU (other
  * streams, other host threads) race and must not be issued; calls on one stream are ordered.
+ * The stream must belong to the current device (the array's address is that device's).
  * Errors: as mla_decode_splitkv and mla_splitkv_combine, plus INVALID_ARG for a NULL
- * out_bf16_dev with B > 0, WORKSPACE as above, HIP if the array's address cannot be found.
+ * out_bf16_dev with B > 0 or a stream of another device, WORKSPACE as above, HIP if the
+ * array's address or the stream's device cannot be found.
  */
 #define MLA_NOALLOC_SCRATCH_BYTES (40 * 1024 * 1024)
 mla_status mla_decode_noalloc(const uint8_t* q8_dev, const uint8_t* kv_pool_dev,

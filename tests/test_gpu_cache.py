@@ -185,6 +185,62 @@ def test_append_rope_bit_exact(t_new, page_size, offset, src, tables):
     assert not np.array_equal(ref[..., 512:], plain[..., 512:])
 
 
+def _append_sweep_cases(n=30, seed=20261206):
+    """Append shapes drawn once: page sizes that are not multiples of the 32-token tile (1, 7,
+    100, 333) beside the usual ones, 1-9 new rows per request, lengths below T, exactly at the
+    table's end and past it, page ids outside the pool, fp32 or bf16 rows, with or without
+    RoPE (tables that may end before some positions)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 6))
+        T = int(rng.integers(1, 10))
+        P = int(rng.choice([1, 7, 32, 64, 100, 333]))
+        max_pages = int(rng.integers(1, 9))
+        cap = max_pages * P
+        lens = [int(rng.choice([rng.integers(0, cap + 1), cap, cap + int(rng.integers(1, 5)),
+                                max(T - int(rng.integers(1, 3)), 0)])) for _ in range(B)]
+        bad = int(rng.integers(0, B)) if rng.random() < 0.4 else None
+        src = "bf16" if rng.random() < 0.4 else "f32"
+        rope = rng.random() < 0.5
+        positions = int(rng.integers(1, cap + 5)) if rope else 0
+        out.append((f"a{i:02d}_b{B}_t{T}_p{P}_m{max_pages}_{src}" + ("_rope" if rope else ""),
+                    B, T, P, max_pages, lens, bad, src, positions, int(rng.integers(0, 1 << 30))))
+    return out
+
+
+APPEND_SWEEP = _append_sweep_cases()
+
+
+@pytest.mark.parametrize("case", APPEND_SWEEP, ids=[c[0] for c in APPEND_SWEEP])
+def test_append_sweep_bit_exact(case):
+    name, B, T, P, max_pages, lens, bad, src, positions, seed = case
+    print(f"[append] {name} lens {lens} bad page request {bad} rope positions {positions}",
+          flush=True)
+    rng = np.random.default_rng(seed)
+    pool, table, seq, new = _append_case(rng, lens, T, P, max_pages, bad_page_req=bad)
+    s = np.float32(2.0 * 4.5 / 448)
+    if src == "bf16":
+        bits = (new.view(np.uint32) >> 16).astype(np.uint16)
+        rows = bf16_bits_to_f32(bits)
+        g_new = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        rows = new
+        g_new = torch.from_numpy(new).cuda()
+    g_pool = torch.from_numpy(pool).cuda()
+    g_table, g_seq = torch.from_numpy(table).cuda(), torch.from_numpy(seq).cuda()
+    if positions:
+        cos_t, sin_t = _rope_tables(rng, positions, "random")
+        ref = append_kv_rope_fp8(pool, table, seq, rows, s, cos_t, sin_t)
+        mla.kv_append_rope_fp8_sat(g_new, g_pool, g_table, g_seq, float(s),
+                                   torch.from_numpy(cos_t).cuda(), torch.from_numpy(sin_t).cuda())
+    else:
+        ref = append_kv_fp8(pool, table, seq, rows, s)
+        mla.kv_append_fp8_sat(g_new, g_pool, g_table, g_seq, float(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(g_pool.cpu().numpy(), ref)
+
+
 def test_append_then_decode_reads_the_new_rows():
     """Step-by-step: a request's last 3 rows are appended (one step at a time) into a cache
     whose first rows came from the plain quantiser; the decode over the result matches the

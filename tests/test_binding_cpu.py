@@ -75,3 +75,24 @@ def test_the_product_never_imports_the_oracle():
         nested = sum(len(list(oracle_imports(fn))) for fn in ast.walk(tree)
                      if isinstance(fn, ast.FunctionDef) and fn.name in allowed)
         assert inside <= allowed and total == nested, (script, inside)
+
+
+def test_a_package_without_its_library_fails_loudly(tmp_path):
+    """No fallback: a copy of the package without libmla.so raises on first use, naming the
+    build step, rather than computing anything another way."""
+    import os
+    import shutil
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    dst = tmp_path / "fp8_mla_split_amd"
+    shutil.copytree(os.path.join(root, "fp8_mla_split_amd"), dst,
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    code = ("import fp8_mla_split_amd as m\n"
+            "try:\n"
+            "    m.decode_splitkv\n"
+            "except ImportError as e:\n"
+            "    print('IMPORT-ERROR', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True,
+                       text=True, timeout=300)
+    assert "IMPORT-ERROR" in r.stdout and "fp8_mla_split_amd.build" in r.stdout, r.stdout + r.stderr
